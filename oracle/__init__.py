@@ -1,0 +1,16 @@
+"""fp64 CPU oracle for paged latent attention.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the library itself.
+"""
+
+from .mla_oracle import (  # noqa: F401
+    attention,
+    attention_loops,
+    gather_row_keys,
+    kv_lengths,
+    merge_state,
+    validate,
+    visible_keys,
+    widen,
+)
