@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Benchmark: paged MLA decode on one MI355X.
+
+One step = one pass of the whole path over one batch: ``mla_plan`` (host
+planning + asynchronous copy of the schedule) followed by ``mla_run``
+(attention kernel + split-KV merge kernel).  The workload is the decode batch
+of 64 rows, 128 heads, page_size 64, kv lengths uniform in [512, 4096]
+(seed 1002), with inputs resident in HBM.  Three independent copies of the KV
+cache, queries and outputs are rotated so the 256 MB last-level cache cannot
+serve a step from the previous one.
+
+``value`` is decode throughput in GB/s of algorithmic bytes (latent rows read
+once, queries read, outputs and LSE written, index arrays) per wall-clock
+step.  The JSON line also carries the chunked-prefill throughput (TFLOP/s),
+the kernel roofline and the fp64 CPU oracle's throughput on this host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+ROW_BYTES = 576 * 2
+FLOPS_PER_PAIR = 2 * 576 + 2 * 512
+
+
+def algorithmic(w, return_lse=True):
+    """Bytes and flops the method must move/compute for workload w."""
+    lens = w.kv_lens()
+    T, H = w.num_tokens, w.num_heads
+    nbytes = ROW_BYTES * int(lens.sum()) + T * H * (576 * 2 + 512 * 2)
+    if return_lse:
+        nbytes += 4 * T * H
+    nbytes += 4 * (2 * (w.batch + 1) + w.batch + int(w.kv_indptr[-1]))
+    pairs = 0
+    qo = w.qo_indptr
+    for b in range(w.batch):
+        Q, L = int(qo[b + 1] - qo[b]), int(lens[b])
+        if w.causal:
+            i = np.arange(Q)
+            pairs += int(np.clip(i + L - Q + 1, 0, L).sum())
+        else:
+            pairs += Q * L
+    return nbytes, FLOPS_PER_PAIR * H * pairs
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_mla_attention_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload_name):
+    """Counter-derived HBM bytes per launch, if measured on the current
+    kernel sources (profiles/traffic.json)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        doc = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    ent = doc.get(workload_name)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def _to_dev_bf16(bits, torch):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).cuda()
+
+
+def run_steps(w, steps, warmup, copies=3):
+    import torch
+
+    import paged_mla_attention_amd as pm
+    T, H = w.num_tokens, w.num_heads
+    kv0 = _to_dev_bf16(w.kv_cache, torch)
+    qn0, qp0 = _to_dev_bf16(w.q_nope, torch), _to_dev_bf16(w.q_pe, torch)
+    kvs = [kv0] + [kv0.clone() for _ in range(copies - 1)]
+    qns = [qn0] + [qn0.clone() for _ in range(copies - 1)]
+    qps = [qp0] + [qp0.clone() for _ in range(copies - 1)]
+    outs = [torch.empty((T, H, 512), dtype=torch.bfloat16, device="cuda") for _ in range(copies)]
+    lses = [torch.empty((T, H), dtype=torch.float32, device="cuda") for _ in range(copies)]
+    plan = pm.MLAPlan(H, w.page_size)
+    qo, kvp, idx, last = (np.ascontiguousarray(a, dtype=np.int32) for a in
+                          (w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_len))
+
+    def step(k, ev=None):
+        plan.plan(qo, kvp, idx, last, causal=w.causal, sm_scale=w.sm_scale,
+                  num_cache_pages=w.num_pages)
+        c = k % copies
+        if ev is not None:
+            ev[0].record()
+        plan.run(qns[c], qps[c], kvs[c], out=outs[c], lse=lses[c])
+        if ev is not None:
+            ev[1].record()
+
+    for k in range(warmup):
+        step(k)
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+    t0 = time.perf_counter()
+    for k in range(steps):
+        step(k, events[k])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    run_ms = float(np.mean([a.elapsed_time(b) for a, b in events]))
+    stats = plan.stats()
+    plan.close()
+    return wall * 1e3, run_ms, stats
+
+
+def cpu_baseline(w, target_s=10.0):
+    """The fp64 oracle on this host's cores over whole repeats of the batch."""
+    import oracle
+    nbytes, _ = algorithmic(w)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.attention(w.q_nope, w.q_pe, w.kv_cache, w.qo_indptr, w.kv_indptr, w.kv_indices,
+                         w.kv_last_page_len, w.page_size, w.causal, w.sm_scale)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s:
+            break
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count()
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    return {"value": round(nbytes * reps / el / 1e9, 3), "unit": "GB/s", "cores": min(cores, threads),
+            "kind": "oracle",
+            "sample": f"whole decode batch (64 rows, H=128) x {reps} repeats, {el:.1f} s, fp64 numpy"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    w = W.decode_batch()
+    nbytes, flops = algorithmic(w)
+    print(f"[bench] decode workload ready: T={w.num_tokens} H={w.num_heads} "
+          f"keys={int(w.kv_lens().sum())}", file=sys.stderr, flush=True)
+    ms_step, run_ms, stats = run_steps(w, args.steps, args.warmup)
+    value = nbytes / (ms_step * 1e-3) / 1e9
+    achieved = nbytes / (run_ms * 1e-3) / 1e9
+    print(f"[bench] decode: {ms_step * 1e3:.1f} us/step, mla_run {run_ms * 1e3:.1f} us",
+          file=sys.stderr, flush=True)
+
+    prefill = None
+    if not args.no_prefill:
+        wp = W.chunked_prefill()
+        pbytes, pflops = algorithmic(wp)
+        print("[bench] prefill workload ready", file=sys.stderr, flush=True)
+        p_ms, p_run_ms, _ = run_steps(wp, max(3, args.steps // 5), 2, copies=1)
+        prefill = {"workload": wp.name, "tflops": round(pflops / (p_ms * 1e-3) / 1e12, 2),
+                   "run_tflops": round(pflops / (p_run_ms * 1e-3) / 1e12, 2),
+                   "ms_per_step": round(p_ms, 4), "run_ms": round(p_run_ms, 4),
+                   "frac_mfma_peak": round(pflops / (p_run_ms * 1e-3) / 1e12
+                                           / MFMA_BF16_PEAK_TFLOPS, 4),
+                   "algorithmic_flops": pflops, "algorithmic_bytes": pbytes}
+        print(f"[bench] prefill: {p_ms:.3f} ms/step", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w)
+
+    line = {
+        "metric": "paged-MLA decode GB/s & prefill TFLOP/s (% MI355X roofline), B=64 H=128",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode B=64 qo_len=1 H=128 kv_lora_rank=512 rope=64 "
+                               "page_size=64 kv~U[512,4096] seed=1002",
+                   "global_batch": w.batch, "seq_len": int(w.kv_lens().mean()),
+                   "tokens_per_s": round(w.num_tokens / (ms_step * 1e-3), 1)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic("decode"),
+                     "kernel": "mla_run (attention_kernel + split_merge_kernel)",
+                     "duration_us": round(run_ms * 1e3, 2), "algorithmic_bytes": nbytes,
+                     "algorithmic_flops": flops, "plan": stats},
+        "prefill": prefill,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

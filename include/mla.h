@@ -1,0 +1,193 @@
+/*
+ * mla.h - paged Multi-head Latent Attention (MLA) for AMD Instinct MI355X
+ * (gfx950).  C ABI: plain pointers and sizes, no framework types.
+ *
+ * What is computed (m-star documentation, page
+ * "mstar.engine.resources.attn.flashinfer_mla": module description and
+ * FlashInferMLAWrapper.plan / run):
+ *
+ *   The cache holds one latent row per token, [ckv (512) | kpe (64)] bf16.
+ *   For query token t of row b, head h, and each key j the row may see,
+ *     s_j = sm_scale * (q_nope[t,h,:] . ckv_j + q_pe[t,h,:] . kpe_j)
+ *     out[t,h,:] = sum_j softmax(s)_j * ckv_j          (latent space, 512 wide)
+ *     lse[t,h]   = ln sum_j exp(s_j)                   (natural log, fp32)
+ *   q_nope is the absorbed query (q_nope @ W_UK, kv_lora_rank wide) and q_pe
+ *   the un-rotated rope part; the kernel applies no rotation and no W_UV.
+ *
+ *   Rows are ragged through a CSR page table (FlashInferMLAWrapper.plan):
+ *     qo_indptr[B+1]        query tokens of row b: [qo_indptr[b], qo_indptr[b+1])
+ *     kv_indptr[B+1]        pages of row b: kv_indices[kv_indptr[b] .. kv_indptr[b+1])
+ *     kv_indices[nnz]       page ids into the cache, in key order
+ *     kv_last_page_len[B]   valid slots of the row's last page, 1..page_size
+ *   so row b holds L_b = (n_b - 1) * page_size + kv_last_page_len[b] keys
+ *   (0 when it names no page).  Key j of the row is slot j % page_size of
+ *   page kv_indices[kv_indptr[b] + j / page_size].
+ *
+ *   Causal (the plan default): a row's query block is aligned to the end of
+ *   its keys (page "mstar.engine.resources.attn.ragged.wrappers",
+ *   PrefixedPrefillWrapper): query i of Q sees keys j <= i + L - Q.  A query
+ *   that sees no key gets out = 0 and lse = -inf.  Non-causal: every query
+ *   sees all L keys.
+ *
+ *   sm_scale is the softmax scale of the original head dim, e.g. 192^-0.5
+ *   (FlashInferMLAWrapper parameters).
+ *
+ * Tensor layouts (all row-major, contiguous, device memory):
+ *   q_nope   bf16 [T, H, 512]     q_pe bf16 [T, H, 64]
+ *   kv_cache bf16 [num_cache_pages, page_size, 576]  (ckv first, then kpe)
+ *   out      bf16 [T, H, 512]     lse  fp32 [T, H]
+ * with T = qo_indptr[B] and H = num_heads.
+ *
+ * Supported shapes: kv_lora_rank 512 and qk_rope_head_dim 64 exactly (the
+ * DeepSeek/Kimi latent shape the flashinfer_mla_supports page names); other
+ * ranks return MLA_E_UNSUPPORTED, there is no fallback path.  1 <= num_heads
+ * <= 128, page_size >= 1.
+ *
+ * Errors: every entry point returns a status; nothing aborts or throws across
+ * the ABI.  mla_last_error() returns a thread-local text for the last failing
+ * call on the calling thread.
+ *
+ * Threading: a plan handle must not be used by two threads at once.
+ * Independent handles never interact.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_E_INVALID = 1,     /* bad argument or page table (message says which) */
+  MLA_E_UNSUPPORTED = 2, /* shape the kernels do not implement */
+  MLA_E_STATE = 3,       /* call order violated, e.g. mla_run before mla_plan */
+  MLA_E_HIP = 4,         /* a HIP runtime call failed (message has the HIP error) */
+  MLA_E_NOMEM = 5        /* device or pinned host allocation failed */
+} mla_status;
+
+/* An opaque plan.  The library owns its pinned staging buffer, its device
+ * copy of the schedule and page table, and its split-KV partial workspace. */
+typedef struct mla_plan_s* mla_plan_t;
+
+/* A HIP stream (hipStream_t); NULL is the null stream. */
+typedef void* mla_stream_t;
+
+/* Create a plan on HIP device `device` for `num_heads` query heads (1..128),
+ * latent shape (kv_lora_rank, qk_rope_head_dim) which must be (512, 64), and
+ * cache pages of `page_size` tokens.  Constructor arguments follow
+ * FlashInferMLAWrapper(num_qo_heads, kv_lora_rank, qk_rope_head_dim,
+ * page_size).  The number of workers is the device's compute-unit count.
+ * On success *out owns the plan; release it with mla_plan_destroy. */
+mla_status mla_plan_create(mla_plan_t* out, int32_t device, int32_t num_heads,
+                           int32_t kv_lora_rank, int32_t qk_rope_head_dim,
+                           int32_t page_size);
+
+/* Plan one batch (FlashInferMLAWrapper.plan): validate the CSR page table,
+ * split each query token's visible keys into chunks balanced over the
+ * compute units, and copy the schedule and page table to the device.
+ *
+ * All four index arrays are HOST int32 memory (the page notes that the KV plan
+ * builds them on the host); they are read before the call returns and not
+ * kept.  kv_indices must hold at least kv_indptr[batch] entries.  Page ids
+ * must lie in [0, num_cache_pages).
+ *
+ * The host-to-device copy is asynchronous on `stream`.  Before it overwrites
+ * its pinned staging buffer, mla_plan waits for the previous plan's copy to
+ * finish, so planning step N+1 never races step N's in-flight copy.  The
+ * first plan, and any plan that outgrows the device buffers, synchronises
+ * `stream` while it (re)allocates; later plans of equal or smaller size
+ * allocate nothing.  mla_run must be called on the same stream (or one
+ * ordered after it).
+ *
+ * Errors: MLA_E_INVALID for a malformed table (indptr[0] != 0, decreasing
+ * indptr, last_page_len outside [1, page_size] on a row with pages, page id
+ * out of range, batch < 0, non-finite or non-positive sm_scale).  The plan
+ * keeps its previous state on error. */
+mla_status mla_plan(mla_plan_t plan, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                    const int32_t* kv_indices, const int32_t* kv_last_page_len,
+                    int32_t batch, int32_t causal, float sm_scale,
+                    int64_t num_cache_pages, mla_stream_t stream);
+
+/* Run the planned batch (FlashInferMLAWrapper.run): all pointers are device
+ * memory with the layouts above; `lse` may be NULL when not wanted.  The call
+ * only enqueues kernels on `stream` (no allocation, no synchronisation), so
+ * it may be captured in a HIP graph.  The plan must not be re-planned while a
+ * captured graph that reads it may still replay.
+ *
+ * Errors: MLA_E_STATE without a successful mla_plan; MLA_E_INVALID for a NULL
+ * required pointer; MLA_E_HIP if a launch fails. */
+mla_status mla_run(mla_plan_t plan, const void* q_nope, const void* q_pe,
+                   const void* kv_cache, void* out, float* lse, mla_stream_t stream);
+
+/* Merge two attention results over disjoint key segments of the same
+ * queries through their LSEs (FlashInferMLAManager.run: the LSE is returned
+ * for merging with another key segment):
+ *   M = max(s_a, s_b);  w_x = exp(s_x - M)
+ *   v_out = (w_a v_a + w_b v_b) / (w_a + w_b),  s_out = M + ln(w_a + w_b)
+ * and (0, -inf) where both sides are empty (-inf).
+ * v_* are bf16 [num_tokens, num_heads, 512], s_* fp32 [num_tokens, num_heads],
+ * device memory; arithmetic in fp32.  v_out / s_out may alias v_a / s_a (or
+ * v_b / s_b) exactly; partial overlap is not allowed.  Enqueued on `stream`,
+ * no allocation or synchronisation. */
+mla_status mla_merge_state(const void* v_a, const float* s_a, const void* v_b,
+                           const float* s_b, void* v_out, float* s_out,
+                           int64_t num_tokens, int32_t num_heads, mla_stream_t stream);
+
+/* Release a plan and everything it owns.  Waits for the plan's pending
+ * copy; the caller must make sure no enqueued mla_run on it is still
+ * executing.  NULL is ignored. */
+void mla_plan_destroy(mla_plan_t plan);
+
+/* Planner introspection for a plan that has been planned: the number of
+ * workers (workgroups) the attention kernel launches, work items, query
+ * tokens whose keys were split over several items, and partial slots.
+ * Any output pointer may be NULL. */
+mla_status mla_plan_stats(mla_plan_t plan, int32_t* num_workers, int64_t* num_items,
+                          int64_t* num_split_tokens, int64_t* num_partials);
+
+/* Static text for a status code. */
+const char* mla_status_str(mla_status status);
+
+/* Detail of the last failing call on this thread ("" if none). */
+const char* mla_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Host-only schedule (no device needed).  The same planner mla_plan runs,
+ * exposed so its output can be inspected and replayed on the CPU.
+ *
+ * Work item (8 int32 each): {token, row, kv_begin, kv_end, slot, 0, 0, 0}:
+ *   query token `token` of row `row` attends the row's keys
+ *   [kv_begin, kv_end); slot = -1 writes the final result, slot >= 0 writes
+ *   a partial result (normalised output and LSE) into partial slot `slot`.
+ * Merge entry (4 int32 each): {token, first_slot, num_slots, 0}: the token's
+ *   result is the LSE merge of partial slots [first_slot, first_slot+num_slots).
+ * worker_indptr[num_workers+1]: worker w (workgroup w of the attention
+ *   launch) runs items [worker_indptr[w], worker_indptr[w+1]) in order.
+ * ------------------------------------------------------------------------ */
+typedef struct mla_schedule_s* mla_schedule_t;
+
+mla_status mla_schedule_build(mla_schedule_t* out, const int32_t* qo_indptr,
+                              const int32_t* kv_indptr, const int32_t* kv_indices,
+                              const int32_t* kv_last_page_len, int32_t batch,
+                              int32_t causal, int32_t page_size, int64_t num_cache_pages,
+                              int32_t num_heads, int32_t num_workers);
+
+/* Sizes of a built schedule; any pointer may be NULL. */
+void mla_schedule_sizes(mla_schedule_t s, int32_t* num_workers, int64_t* num_items,
+                        int64_t* num_merges, int64_t* num_slots);
+
+/* Copy the schedule out: worker_indptr [num_workers+1], items [num_items*8],
+ * merges [num_merges*4] (host memory, sized from mla_schedule_sizes). */
+void mla_schedule_copy(mla_schedule_t s, int32_t* worker_indptr, int32_t* items,
+                       int32_t* merges);
+
+void mla_schedule_destroy(mla_schedule_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

@@ -1,0 +1,255 @@
+"""Paged Multi-head Latent Attention for AMD MI355X (gfx950).
+
+A thin Python binding over the C ABI of ``libmla.so`` (include/mla.h).  It
+only marshals arguments: every step of the attention runs in the library's
+HIP kernels; PyTorch supplies device memory and streams.  The functions keep
+the C names (``mla_plan_create``, ``mla_plan``, ``mla_run``,
+``mla_merge_state``, ``mla_plan_destroy``); :class:`MLAPlan` bundles them.
+
+Interface after the m-star page "mstar.engine.resources.attn.flashinfer_mla"
+(FlashInferMLAWrapper: constructor, plan, run).
+"""
+
+from __future__ import annotations
+
+import ctypes
+from ctypes import c_int32, c_int64, c_void_p
+from typing import Optional
+
+import numpy as np
+
+from . import _native
+
+KV_LORA_RANK = 512
+QK_ROPE_HEAD_DIM = 64
+
+__all__ = [
+    "MLAPlan", "mla_plan_create", "mla_plan", "mla_run", "mla_merge_state",
+    "mla_plan_destroy", "mla_plan_stats", "merge_state", "schedule", "library",
+]
+
+
+def library():
+    """The loaded product library (raises if it is not built)."""
+    return _native.load(_native.LIB_PATH)
+
+
+def _host_i32(x) -> np.ndarray:
+    """Index arrays are read on the host.  A GPU tensor costs a device sync."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().to("cpu").numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x), dtype=np.int32)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(c_int32))
+
+
+def _stream_handle(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dev_ptr(t, name, dtype, shape):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+# ----------------------------------------------------------------------------
+# C-named functions
+# ----------------------------------------------------------------------------
+
+def mla_plan_create(device: int, num_heads: int, kv_lora_rank: int = KV_LORA_RANK,
+                    qk_rope_head_dim: int = QK_ROPE_HEAD_DIM, page_size: int = 64) -> int:
+    lib = library()
+    h = c_void_p()
+    _native.check(lib, lib.mla_plan_create(ctypes.byref(h), device, num_heads, kv_lora_rank,
+                                           qk_rope_head_dim, page_size))
+    return h.value
+
+
+def mla_plan(handle: int, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, causal: bool,
+             sm_scale: float, num_cache_pages: int, stream: int) -> None:
+    lib = library()
+    qo, kv = _host_i32(qo_indptr), _host_i32(kv_indptr)
+    idx, last = _host_i32(kv_indices), _host_i32(kv_last_page_len)
+    batch = qo.shape[0] - 1
+    if kv.shape[0] != batch + 1 or last.shape[0] != batch:
+        raise ValueError("qo_indptr, kv_indptr and kv_last_page_len disagree on the batch size")
+    if idx.size == 0:
+        idx = np.zeros(1, np.int32)
+    _native.check(lib, lib.mla_plan(handle, _ptr(qo), _ptr(kv), _ptr(idx), _ptr(last), batch,
+                                    1 if causal else 0, float(sm_scale), int(num_cache_pages),
+                                    stream))
+
+
+def mla_run(handle: int, q_nope_ptr: int, q_pe_ptr: int, kv_cache_ptr: int, out_ptr: int,
+            lse_ptr: Optional[int], stream: int) -> None:
+    lib = library()
+    _native.check(lib, lib.mla_run(handle, q_nope_ptr, q_pe_ptr, kv_cache_ptr, out_ptr,
+                                   lse_ptr, stream))
+
+
+def mla_merge_state(v_a: int, s_a: int, v_b: int, s_b: int, v_out: int, s_out: int,
+                    num_tokens: int, num_heads: int, stream: int) -> None:
+    lib = library()
+    _native.check(lib, lib.mla_merge_state(v_a, s_a, v_b, s_b, v_out, s_out, num_tokens,
+                                           num_heads, stream))
+
+
+def mla_plan_destroy(handle: int) -> None:
+    if handle:
+        library().mla_plan_destroy(handle)
+
+
+def mla_plan_stats(handle: int) -> dict:
+    lib = library()
+    w, n, s, p = c_int32(), c_int64(), c_int64(), c_int64()
+    _native.check(lib, lib.mla_plan_stats(handle, ctypes.byref(w), ctypes.byref(n),
+                                          ctypes.byref(s), ctypes.byref(p)))
+    return {"num_workers": w.value, "num_items": n.value, "num_split_tokens": s.value,
+            "num_partials": p.value}
+
+
+# ----------------------------------------------------------------------------
+# Torch-facing wrapper
+# ----------------------------------------------------------------------------
+
+class MLAPlan:
+    """One plan handle: ``plan(...)`` on host index arrays, then ``run(...)``.
+
+    Mirrors FlashInferMLAWrapper(num_qo_heads, kv_lora_rank, qk_rope_head_dim,
+    page_size) with ``plan(qo_indptr, paged_kv_indptr, paged_kv_indices,
+    paged_kv_last_page_len, causal=True)`` and ``run(q_nope, q_pe,
+    kv_cache_layer, return_lse=False)``.
+    """
+
+    def __init__(self, num_heads: int, page_size: int, kv_lora_rank: int = KV_LORA_RANK,
+                 qk_rope_head_dim: int = QK_ROPE_HEAD_DIM, device: Optional[int] = None):
+        import torch
+        if device is None:
+            device = torch.cuda.current_device()
+        self.device = int(device)
+        self.num_heads = int(num_heads)
+        self.page_size = int(page_size)
+        self._h = mla_plan_create(self.device, self.num_heads, kv_lora_rank, qk_rope_head_dim,
+                                  self.page_size)
+        self._planned = None
+
+    def plan(self, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, causal: bool = True,
+             sm_scale: float = 192.0 ** -0.5, num_cache_pages: Optional[int] = None,
+             stream=None) -> None:
+        qo = _host_i32(qo_indptr)
+        if num_cache_pages is None:
+            raise ValueError("num_cache_pages is required (page ids are validated against it)")
+        mla_plan(self._h, qo, kv_indptr, kv_indices, kv_last_page_len, causal, sm_scale,
+                 num_cache_pages, _stream_handle(stream))
+        self._planned = (int(qo[-1]), int(num_cache_pages))
+
+    def run(self, q_nope, q_pe, kv_cache, return_lse: bool = False, out=None, lse=None,
+            stream=None):
+        import torch
+        if self._planned is None:
+            raise RuntimeError("run() before plan()")
+        T, pages = self._planned
+        H = self.num_heads
+        if kv_cache.dim() != 3 or kv_cache.shape[0] < pages:
+            raise ValueError(f"kv_cache must be [>= {pages}, page_size, 576]")
+        qn = _dev_ptr(q_nope, "q_nope", torch.bfloat16, (T, H, KV_LORA_RANK))
+        qp = _dev_ptr(q_pe, "q_pe", torch.bfloat16, (T, H, QK_ROPE_HEAD_DIM))
+        kv = _dev_ptr(kv_cache, "kv_cache", torch.bfloat16,
+                      (kv_cache.shape[0], self.page_size, KV_LORA_RANK + QK_ROPE_HEAD_DIM))
+        if out is None:
+            out = torch.empty((T, H, KV_LORA_RANK), dtype=torch.bfloat16, device=q_nope.device)
+        op = _dev_ptr(out, "out", torch.bfloat16, (T, H, KV_LORA_RANK))
+        lp = None
+        if return_lse or lse is not None:
+            if lse is None:
+                lse = torch.empty((T, H), dtype=torch.float32, device=q_nope.device)
+            lp = _dev_ptr(lse, "lse", torch.float32, (T, H))
+        mla_run(self._h, qn, qp, kv, op, lp, _stream_handle(stream))
+        return (out, lse) if (return_lse or lp is not None) else out
+
+    def stats(self) -> dict:
+        return mla_plan_stats(self._h)
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            mla_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):  # pragma: no cover
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def merge_state(v_a, s_a, v_b, s_b, v_out=None, s_out=None, stream=None):
+    """LSE merge of two results over disjoint key segments (bf16 v, fp32 s)."""
+    import torch
+    if v_a.dim() != 3 or v_a.shape[-1] != KV_LORA_RANK:
+        raise ValueError("v_a must be [T, H, 512]")
+    T, H = int(v_a.shape[0]), int(v_a.shape[1])
+    if v_out is None:
+        v_out = torch.empty_like(v_a)
+    if s_out is None:
+        s_out = torch.empty_like(s_a)
+    ptrs = [
+        _dev_ptr(v_a, "v_a", torch.bfloat16, (T, H, KV_LORA_RANK)),
+        _dev_ptr(s_a, "s_a", torch.float32, (T, H)),
+        _dev_ptr(v_b, "v_b", torch.bfloat16, (T, H, KV_LORA_RANK)),
+        _dev_ptr(s_b, "s_b", torch.float32, (T, H)),
+        _dev_ptr(v_out, "v_out", torch.bfloat16, (T, H, KV_LORA_RANK)),
+        _dev_ptr(s_out, "s_out", torch.float32, (T, H)),
+    ]
+    mla_merge_state(*ptrs, T, H, _stream_handle(stream))
+    return v_out, s_out
+
+
+# ----------------------------------------------------------------------------
+# Host-only planner output (no GPU needed)
+# ----------------------------------------------------------------------------
+
+def schedule(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, page_size: int,
+             num_cache_pages: int, num_heads: int, num_workers: int, causal: bool = True,
+             lib_path: Optional[str] = None) -> dict:
+    """Run the host planner and return its schedule as numpy arrays."""
+    lib = _native.load(lib_path or _native.LIB_PATH, host_only=True)
+    qo, kv = _host_i32(qo_indptr), _host_i32(kv_indptr)
+    idx, last = _host_i32(kv_indices), _host_i32(kv_last_page_len)
+    if idx.size == 0:
+        idx = np.zeros(1, np.int32)
+    h = c_void_p()
+    _native.check(lib, lib.mla_schedule_build(ctypes.byref(h), _ptr(qo), _ptr(kv), _ptr(idx),
+                                              _ptr(last), qo.shape[0] - 1, 1 if causal else 0,
+                                              page_size, num_cache_pages, num_heads, num_workers))
+    try:
+        w, n, m, s = c_int32(), c_int64(), c_int64(), c_int64()
+        lib.mla_schedule_sizes(h, ctypes.byref(w), ctypes.byref(n), ctypes.byref(m),
+                               ctypes.byref(s))
+        wi = np.zeros(w.value + 1, np.int32)
+        items = np.zeros((n.value, 8), np.int32)
+        merges = np.zeros((m.value, 4), np.int32)
+        lib.mla_schedule_copy(h, _ptr(wi), _ptr(items), _ptr(merges))
+    finally:
+        lib.mla_schedule_destroy(h)
+    return {"worker_indptr": wi, "items": items, "merges": merges, "num_slots": s.value}

@@ -1,0 +1,293 @@
+// C ABI of the library (include/mla.h): plan objects, the host-to-device
+// schedule copy with its staging fence, and the kernel launches.
+//
+// The staging fence follows the hazard the m-star page
+// "mstar.engine.resources.attn.flashinfer_mla" describes under
+// FlashInferMLAManager.force_double_buffer: a plan that stages into a reused
+// host buffer and copies it to the device without blocking must not
+// overwrite that buffer before the previous copy has been consumed.  Here
+// every plan waits on the event recorded after its previous copy.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "kernels.h"
+#include "planner.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+mla_status hip_fail(hipError_t e, const char* what) {
+  char buf[256];
+  std::snprintf(buf, sizeof buf, "%s: %s", what, hipGetErrorString(e));
+  mla::set_last_error(buf);
+  return e == hipErrorOutOfMemory ? MLA_E_NOMEM : MLA_E_HIP;
+}
+
+mla_status fail(mla_status s, const char* msg) {
+  mla::set_last_error(msg);
+  return s;
+}
+
+// Makes `dev` current for the scope and restores the caller's device.
+struct DeviceGuard {
+  int prev = -1;
+  hipError_t err = hipSuccess;
+  explicit DeviceGuard(int dev) {
+    err = hipGetDevice(&prev);
+    if (err == hipSuccess && prev != dev) err = hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+}  // namespace
+
+struct mla_plan_s {
+  int device = 0;
+  int num_heads = 0;
+  int page_size = 0;
+  int num_workers = 0;
+
+  bool planned = false;
+  float scale_log2 = 0.f;
+  mla::Schedule sched;
+
+  // Pinned host staging and its device mirror: worker_indptr | items |
+  // merges | kv_indptr | kv_indices, each section 256-byte aligned.
+  char* h_stage = nullptr;
+  size_t h_stage_cap = 0;
+  char* d_stage = nullptr;
+  size_t d_stage_cap = 0;
+  size_t off_items = 0, off_merges = 0, off_kv_indptr = 0, off_kv_indices = 0;
+
+  // Split-KV partials: fp32 o [slots, H, 512] then lse [slots, H].
+  float* d_part = nullptr;
+  size_t part_cap = 0;  // floats
+
+  hipEvent_t h2d_done = nullptr;
+  bool h2d_pending = false;
+};
+
+extern "C" {
+
+mla_status mla_plan_create(mla_plan_t* out, int32_t device, int32_t num_heads,
+                           int32_t kv_lora_rank, int32_t qk_rope_head_dim, int32_t page_size) {
+  mla::clear_last_error();
+  if (!out) return fail(MLA_E_INVALID, "NULL output handle");
+  *out = nullptr;
+  if (kv_lora_rank != mla::kLoraRank || qk_rope_head_dim != mla::kRopeDim)
+    return fail(MLA_E_UNSUPPORTED, "only kv_lora_rank 512 with qk_rope_head_dim 64 is supported");
+  if (num_heads < 1 || num_heads > mla::kMaxHeads)
+    return fail(MLA_E_UNSUPPORTED, "num_heads must be in [1, 128]");
+  if (page_size < 1) return fail(MLA_E_INVALID, "page_size must be >= 1");
+  int count = 0;
+  hipError_t e = hipGetDeviceCount(&count);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
+  if (device < 0 || device >= count) return fail(MLA_E_INVALID, "device index out of range");
+  DeviceGuard g(device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+  auto* p = new (std::nothrow) mla_plan_s;
+  if (!p) return fail(MLA_E_NOMEM, "host allocation failed");
+  p->device = device;
+  p->num_heads = num_heads;
+  p->page_size = page_size;
+  p->num_workers = cus > 0 ? cus : 1;
+  e = hipEventCreateWithFlags(&p->h2d_done, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    delete p;
+    return hip_fail(e, "hipEventCreate");
+  }
+  *out = p;
+  return MLA_OK;
+}
+
+mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                    const int32_t* kv_indices, const int32_t* kv_last_page_len, int32_t batch,
+                    int32_t causal, float sm_scale, int64_t num_cache_pages,
+                    mla_stream_t stream_) {
+  mla::clear_last_error();
+  if (!p) return fail(MLA_E_INVALID, "NULL plan");
+  if (!(std::isfinite(sm_scale) && sm_scale > 0.f))
+    return fail(MLA_E_INVALID, "sm_scale must be finite and positive");
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  mla::PlanArgs args{qo_indptr, kv_indptr, kv_indices, kv_last_page_len, batch, causal != 0,
+                     p->page_size, num_cache_pages, p->num_heads, p->num_workers};
+  mla::Schedule s;
+  mla_status st;
+  try {
+    st = mla::build_schedule(args, &s);
+  } catch (const std::bad_alloc&) {
+    st = fail(MLA_E_NOMEM, "host allocation failed");
+  }
+  if (st != MLA_OK) return st;
+
+  DeviceGuard g(p->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+
+  const size_t n_wi = s.worker_indptr.size() * sizeof(int32_t);
+  const size_t n_items = s.items.size() * sizeof(mla::WorkItem);
+  const size_t n_merges = s.merges.size() * sizeof(mla::MergeItem);
+  const size_t n_kvp = static_cast<size_t>(s.batch + 1) * sizeof(int32_t);
+  const size_t n_idx = static_cast<size_t>(s.nnz) * sizeof(int32_t);
+  const size_t off_items = align_up(n_wi);
+  const size_t off_merges = off_items + align_up(n_items);
+  const size_t off_kvp = off_merges + align_up(n_merges);
+  const size_t off_idx = off_kvp + align_up(n_kvp);
+  const size_t total = off_idx + align_up(n_idx);
+
+  // The previous copy must have read the staging buffer before we refill it.
+  hipError_t e;
+  if (p->h2d_pending) {
+    e = hipEventSynchronize(p->h2d_done);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    p->h2d_pending = false;
+  }
+  if (total > p->h_stage_cap) {
+    if (p->h_stage) (void)hipHostFree(p->h_stage);
+    p->h_stage = nullptr;
+    p->h_stage_cap = 0;
+    e = hipHostMalloc(reinterpret_cast<void**>(&p->h_stage), total, hipHostMallocDefault);
+    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc");
+    p->h_stage_cap = total;
+  }
+  const size_t part_floats =
+      static_cast<size_t>(s.num_slots) * p->num_heads * (mla::kLoraRank + 1);
+  if (total > p->d_stage_cap || part_floats > p->part_cap) {
+    // Buffers may still be read by enqueued kernels of an earlier plan.
+    e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+    if (total > p->d_stage_cap) {
+      if (p->d_stage) (void)hipFree(p->d_stage);
+      p->d_stage = nullptr;
+      p->d_stage_cap = 0;
+      e = hipMalloc(reinterpret_cast<void**>(&p->d_stage), total);
+      if (e != hipSuccess) return hip_fail(e, "hipMalloc(schedule)");
+      p->d_stage_cap = total;
+    }
+    if (part_floats > p->part_cap) {
+      if (p->d_part) (void)hipFree(p->d_part);
+      p->d_part = nullptr;
+      p->part_cap = 0;
+      e = hipMalloc(reinterpret_cast<void**>(&p->d_part), part_floats * sizeof(float));
+      if (e != hipSuccess) return hip_fail(e, "hipMalloc(partials)");
+      p->part_cap = part_floats;
+    }
+  }
+  std::memcpy(p->h_stage, s.worker_indptr.data(), n_wi);
+  if (n_items) std::memcpy(p->h_stage + off_items, s.items.data(), n_items);
+  if (n_merges) std::memcpy(p->h_stage + off_merges, s.merges.data(), n_merges);
+  if (s.batch > 0) std::memcpy(p->h_stage + off_kvp, kv_indptr, n_kvp);
+  if (n_idx) std::memcpy(p->h_stage + off_idx, kv_indices, n_idx);
+  e = hipMemcpyAsync(p->d_stage, p->h_stage, total, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+  e = hipEventRecord(p->h2d_done, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  p->h2d_pending = true;
+
+  p->off_items = off_items;
+  p->off_merges = off_merges;
+  p->off_kv_indptr = off_kvp;
+  p->off_kv_indices = off_idx;
+  p->scale_log2 = sm_scale * 1.44269504088896340736f;
+  p->sched = std::move(s);
+  p->planned = true;
+  return MLA_OK;
+}
+
+mla_status mla_run(mla_plan_t p, const void* q_nope, const void* q_pe, const void* kv_cache,
+                   void* out, float* lse, mla_stream_t stream_) {
+  mla::clear_last_error();
+  if (!p) return fail(MLA_E_INVALID, "NULL plan");
+  if (!p->planned) return fail(MLA_E_STATE, "mla_run before a successful mla_plan");
+  const auto& s = p->sched;
+  if (s.num_tokens == 0) return MLA_OK;
+  if (!q_nope || !q_pe || !out) return fail(MLA_E_INVALID, "NULL q_nope, q_pe or out");
+  if (!kv_cache && s.nnz > 0) return fail(MLA_E_INVALID, "NULL kv_cache");
+  DeviceGuard g(p->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+
+  const size_t slots_h = static_cast<size_t>(s.num_slots) * p->num_heads;
+  mla::AttnArgs a{};
+  a.q_nope = static_cast<const uint16_t*>(q_nope);
+  a.q_pe = static_cast<const uint16_t*>(q_pe);
+  a.kv_cache = static_cast<const uint16_t*>(kv_cache);
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.part_o = p->d_part;
+  a.part_lse = p->d_part ? p->d_part + slots_h * mla::kLoraRank : nullptr;
+  a.worker_indptr = reinterpret_cast<const int32_t*>(p->d_stage);
+  a.items = reinterpret_cast<const mla::WorkItem*>(p->d_stage + p->off_items);
+  a.kv_indptr = reinterpret_cast<const int32_t*>(p->d_stage + p->off_kv_indptr);
+  a.kv_indices = reinterpret_cast<const int32_t*>(p->d_stage + p->off_kv_indices);
+  a.num_heads = p->num_heads;
+  a.page_size = p->page_size;
+  a.scale_log2 = p->scale_log2;
+  hipError_t e = mla::launch_attention(a, s.num_workers, stream);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  if (!s.merges.empty()) {
+    mla::SplitMergeArgs m{};
+    m.part_o = a.part_o;
+    m.part_lse = a.part_lse;
+    m.merges = reinterpret_cast<const mla::MergeItem*>(p->d_stage + p->off_merges);
+    m.out = a.out;
+    m.lse = lse;
+    m.num_heads = p->num_heads;
+    m.num_merges = static_cast<int32_t>(s.merges.size());
+    e = mla::launch_split_merge(m, stream);
+    if (e != hipSuccess) return hip_fail(e, "split-merge launch");
+  }
+  return MLA_OK;
+}
+
+mla_status mla_merge_state(const void* v_a, const float* s_a, const void* v_b, const float* s_b,
+                           void* v_out, float* s_out, int64_t num_tokens, int32_t num_heads,
+                           mla_stream_t stream) {
+  mla::clear_last_error();
+  if (num_tokens < 0 || num_heads < 1) return fail(MLA_E_INVALID, "bad num_tokens / num_heads");
+  if (num_tokens == 0) return MLA_OK;
+  if (!v_a || !s_a || !v_b || !s_b || !v_out || !s_out)
+    return fail(MLA_E_INVALID, "NULL pointer");
+  hipError_t e = mla::launch_merge_state(
+      static_cast<const uint16_t*>(v_a), s_a, static_cast<const uint16_t*>(v_b), s_b,
+      static_cast<uint16_t*>(v_out), s_out, num_tokens, num_heads,
+      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "merge_state launch");
+  return MLA_OK;
+}
+
+void mla_plan_destroy(mla_plan_t p) {
+  if (!p) return;
+  DeviceGuard g(p->device);
+  if (p->h2d_pending) (void)hipEventSynchronize(p->h2d_done);
+  if (p->h2d_done) (void)hipEventDestroy(p->h2d_done);
+  if (p->h_stage) (void)hipHostFree(p->h_stage);
+  if (p->d_stage) (void)hipFree(p->d_stage);
+  if (p->d_part) (void)hipFree(p->d_part);
+  delete p;
+}
+
+mla_status mla_plan_stats(mla_plan_t p, int32_t* num_workers, int64_t* num_items,
+                          int64_t* num_split_tokens, int64_t* num_partials) {
+  mla::clear_last_error();
+  if (!p) return fail(MLA_E_INVALID, "NULL plan");
+  if (!p->planned) return fail(MLA_E_STATE, "plan has not been planned");
+  if (num_workers) *num_workers = p->sched.num_workers;
+  if (num_items) *num_items = static_cast<int64_t>(p->sched.items.size());
+  if (num_split_tokens) *num_split_tokens = static_cast<int64_t>(p->sched.merges.size());
+  if (num_partials) *num_partials = p->sched.num_slots;
+  return MLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,309 @@
+// Host planner: page-table validation and split-KV work balancing.
+//
+// The documentation describes planning on the host from CPU index tensors
+// (page "mstar.engine.resources.attn.flashinfer_mla", FlashInferMLAWrapper.plan:
+// "inputs may be CPU tensors") and a per-row key length built from
+// paged_kv_indptr and paged_kv_last_page_len.  The split of long key ranges
+// into chunks, and their balance over compute units, is this library's own
+// design: the work is laid out as one stream of (token, key tile) units and
+// cut into num_workers contiguous pieces of near-equal cost; a token whose
+// keys straddle a cut is split into partial results that a merge kernel
+// combines through their log-sum-exp.
+#include "planner.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+
+namespace mla {
+
+namespace {
+thread_local std::string g_last_error;
+
+struct TokenWork {
+  int32_t token;
+  int32_t row;
+  int32_t visible;  // keys the token sees (a prefix of its row's keys)
+  int32_t tiles;    // ceil(visible / kTileKeys)
+};
+
+// Cost of one work item in units of one key tile (32 latent rows, 36 KiB).
+// Loading the query of all heads costs about four tiles at 128 heads; a
+// partial result (fp32 output of all heads, written once and read back by the
+// merge) costs about seven.
+struct CostModel {
+  double item;
+  double split;
+  explicit CostModel(int heads)
+      : item(1.0 + 4.0 * heads / 128.0), split(1.0 + 7.0 * heads / 128.0) {}
+};
+
+constexpr int kMinPieceTiles = 2;
+
+// Greedy contiguous fill of `budget` cost per worker.  Returns the number of
+// workers used (may exceed num_workers only if forced onto the last one,
+// which is signalled through *overflow).
+void fill(const std::vector<TokenWork>& toks, const CostModel& cm, double budget,
+          int32_t num_workers, std::vector<std::vector<WorkItem>>* per_worker,
+          double* max_load) {
+  per_worker->assign(num_workers, {});
+  std::vector<double> load(num_workers, 0.0);
+  int k = 0;
+  for (const TokenWork& tw : toks) {
+    if (tw.tiles == 0) {
+      (*per_worker)[k].push_back(WorkItem{tw.token, tw.row, 0, 0, -1, {0, 0, 0}});
+      load[k] += cm.item;
+      if (load[k] >= budget && k < num_workers - 1) ++k;
+      continue;
+    }
+    int a = 0;
+    bool split = false;
+    while (a < tw.tiles) {
+      const int rem = tw.tiles - a;
+      const double whole_cost = rem + cm.item + (split ? cm.split : 0.0);
+      const double free = budget - load[k];
+      if (whole_cost <= free + kMinPieceTiles || k == num_workers - 1) {
+        const int32_t kb = a * kTileKeys;
+        (*per_worker)[k].push_back(WorkItem{tw.token, tw.row, kb, tw.visible, split ? 0 : -1, {0, 0, 0}});
+        load[k] += whole_cost;
+        a = tw.tiles;
+        break;
+      }
+      const double space = free - cm.item - cm.split;
+      if (space >= kMinPieceTiles && rem - static_cast<int>(space) >= kMinPieceTiles) {
+        const int take = static_cast<int>(space);
+        const int32_t kb = a * kTileKeys;
+        (*per_worker)[k].push_back(
+            WorkItem{tw.token, tw.row, kb, (a + take) * kTileKeys, 0, {0, 0, 0}});
+        load[k] += take + cm.item + cm.split;
+        a += take;
+        split = true;
+      }
+      ++k;  // this worker is full
+    }
+    if (load[k] >= budget && k < num_workers - 1) ++k;
+  }
+  *max_load = 0.0;
+  for (double l : load) *max_load = std::max(*max_load, l);
+}
+
+}  // namespace
+
+void set_last_error(const std::string& msg) { g_last_error = msg; }
+void clear_last_error() { g_last_error.clear(); }
+
+static mla_status fail(mla_status s, const std::string& msg) {
+  set_last_error(msg);
+  return s;
+}
+
+mla_status build_schedule(const PlanArgs& a, Schedule* out) {
+  char buf[256];
+  if (a.batch < 0) return fail(MLA_E_INVALID, "batch must be >= 0");
+  if (a.page_size < 1) return fail(MLA_E_INVALID, "page_size must be >= 1");
+  if (a.num_heads < 1 || a.num_heads > kMaxHeads)
+    return fail(MLA_E_UNSUPPORTED, "num_heads must be in [1, 128]");
+  if (a.num_workers < 1) return fail(MLA_E_INVALID, "num_workers must be >= 1");
+  if (a.batch > 0 && (!a.qo_indptr || !a.kv_indptr || !a.kv_last_page_len))
+    return fail(MLA_E_INVALID, "NULL index array");
+  if (a.num_cache_pages < 0) return fail(MLA_E_INVALID, "num_cache_pages must be >= 0");
+
+  const int32_t B = a.batch;
+  if (B > 0 && (a.qo_indptr[0] != 0 || a.kv_indptr[0] != 0))
+    return fail(MLA_E_INVALID, "qo_indptr[0] and kv_indptr[0] must be 0");
+  for (int32_t b = 0; b < B; ++b) {
+    if (a.qo_indptr[b + 1] < a.qo_indptr[b]) {
+      std::snprintf(buf, sizeof buf, "qo_indptr decreases at row %d", b);
+      return fail(MLA_E_INVALID, buf);
+    }
+    if (a.kv_indptr[b + 1] < a.kv_indptr[b]) {
+      std::snprintf(buf, sizeof buf, "kv_indptr decreases at row %d", b);
+      return fail(MLA_E_INVALID, buf);
+    }
+    const int32_t n = a.kv_indptr[b + 1] - a.kv_indptr[b];
+    const int32_t last = a.kv_last_page_len[b];
+    if (n > 0 && (last < 1 || last > a.page_size)) {
+      std::snprintf(buf, sizeof buf, "kv_last_page_len[%d]=%d outside [1, %d]", b, last,
+                    a.page_size);
+      return fail(MLA_E_INVALID, buf);
+    }
+    const int64_t L = n > 0 ? int64_t(n - 1) * a.page_size + last : 0;
+    if (L > INT32_MAX / 2) {
+      std::snprintf(buf, sizeof buf, "row %d has too many keys", b);
+      return fail(MLA_E_INVALID, buf);
+    }
+  }
+  const int64_t nnz = B > 0 ? a.kv_indptr[B] : 0;
+  if (nnz > 0 && !a.kv_indices) return fail(MLA_E_INVALID, "NULL kv_indices");
+  for (int64_t i = 0; i < nnz; ++i) {
+    const int32_t p = a.kv_indices[i];
+    if (p < 0 || p >= a.num_cache_pages) {
+      std::snprintf(buf, sizeof buf, "kv_indices[%lld]=%d outside [0, %lld)", (long long)i, p,
+                    (long long)a.num_cache_pages);
+      return fail(MLA_E_INVALID, buf);
+    }
+  }
+  const int64_t T = B > 0 ? a.qo_indptr[B] : 0;
+
+  std::vector<TokenWork> toks;
+  toks.reserve(static_cast<size_t>(T));
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t n = a.kv_indptr[b + 1] - a.kv_indptr[b];
+    const int64_t L = n > 0 ? int64_t(n - 1) * a.page_size + a.kv_last_page_len[b] : 0;
+    const int32_t Q = a.qo_indptr[b + 1] - a.qo_indptr[b];
+    for (int32_t i = 0; i < Q; ++i) {
+      int64_t vis = L;
+      if (a.causal) vis = std::min<int64_t>(L, std::max<int64_t>(0, int64_t(i) + L - Q + 1));
+      const int32_t v = static_cast<int32_t>(vis);
+      toks.push_back(TokenWork{a.qo_indptr[b] + i, b, v, (v + kTileKeys - 1) / kTileKeys});
+    }
+  }
+
+  const CostModel cm(a.num_heads);
+  double total = 0.0;
+  for (const TokenWork& tw : toks) total += tw.tiles + cm.item;
+  const int32_t W = a.num_workers;
+  // Smallest per-worker budget whose greedy fill fits on W workers (split
+  // costs are only known after a fill, so search for it).
+  std::vector<std::vector<WorkItem>> per_worker;
+  double max_load = 0.0;
+  double lo = std::max(total / W, 4.0 + cm.item);
+  double hi = lo;
+  auto fits = [&](double budget) {
+    fill(toks, cm, budget, W, &per_worker, &max_load);
+    return max_load <= budget + kMinPieceTiles;
+  };
+  while (!fits(hi)) hi *= 1.25;
+  for (int iter = 0; iter < 24 && hi - lo > 0.5; ++iter) {
+    const double mid = 0.5 * (lo + hi);
+    if (fits(mid)) hi = mid; else lo = mid;
+  }
+  fill(toks, cm, hi, W, &per_worker, &max_load);
+
+  // Partial slots: tokens that ended up in more than one item.
+  std::vector<int32_t> pieces(static_cast<size_t>(T), 0);
+  for (auto& lst : per_worker)
+    for (WorkItem& it : lst) ++pieces[it.token];
+  std::vector<int32_t> first_slot(static_cast<size_t>(T), -1);
+  std::vector<int32_t> next_slot(static_cast<size_t>(T), 0);
+  Schedule s;
+  int64_t slots = 0;
+  for (int64_t t = 0; t < T; ++t) {
+    if (pieces[t] > 1) {
+      first_slot[t] = static_cast<int32_t>(slots);
+      s.merges.push_back(MergeItem{static_cast<int32_t>(t), static_cast<int32_t>(slots), pieces[t], 0});
+      slots += pieces[t];
+    }
+  }
+  for (auto& lst : per_worker)
+    for (WorkItem& it : lst) {
+      if (pieces[it.token] > 1) {
+        it.slot = first_slot[it.token] + next_slot[it.token]++;
+      } else {
+        it.slot = -1;
+      }
+    }
+
+  // Launch order: workgroups are dispatched round-robin over the 8 XCDs of
+  // the device (each with its own L2), so consecutive logical workers (which
+  // hold neighbouring tokens of the same row, and thus the same keys) are
+  // placed on the same XCD.
+  constexpr int kXcds = 8;
+  std::vector<int32_t> logical_of(W);
+  if (W % kXcds == 0) {
+    const int per = W / kXcds;
+    for (int p = 0; p < W; ++p) logical_of[p] = (p % kXcds) * per + p / kXcds;
+  } else {
+    for (int p = 0; p < W; ++p) logical_of[p] = p;
+  }
+  s.worker_indptr.assign(W + 1, 0);
+  for (int p = 0; p < W; ++p) {
+    const auto& lst = per_worker[logical_of[p]];
+    s.worker_indptr[p + 1] = s.worker_indptr[p] + static_cast<int32_t>(lst.size());
+    s.items.insert(s.items.end(), lst.begin(), lst.end());
+  }
+  s.num_workers = W;
+  s.batch = B;
+  s.num_tokens = T;
+  s.num_slots = slots;
+  s.nnz = nnz;
+  *out = std::move(s);
+  return MLA_OK;
+}
+
+}  // namespace mla
+
+// ---------------------------------------------------------------------------
+// C ABI: host-only schedule, status strings, last error.
+// ---------------------------------------------------------------------------
+
+struct mla_schedule_s {
+  mla::Schedule s;
+};
+
+extern "C" {
+
+const char* mla_status_str(mla_status status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_E_INVALID: return "invalid argument";
+    case MLA_E_UNSUPPORTED: return "unsupported shape";
+    case MLA_E_STATE: return "invalid call order";
+    case MLA_E_HIP: return "HIP runtime error";
+    case MLA_E_NOMEM: return "out of memory";
+  }
+  return "unknown status";
+}
+
+const char* mla_last_error(void) { return mla::g_last_error.c_str(); }
+
+mla_status mla_schedule_build(mla_schedule_t* out, const int32_t* qo_indptr,
+                              const int32_t* kv_indptr, const int32_t* kv_indices,
+                              const int32_t* kv_last_page_len, int32_t batch, int32_t causal,
+                              int32_t page_size, int64_t num_cache_pages, int32_t num_heads,
+                              int32_t num_workers) {
+  mla::clear_last_error();
+  if (!out) return mla::fail(MLA_E_INVALID, "NULL output handle");
+  mla::PlanArgs a{qo_indptr, kv_indptr, kv_indices, kv_last_page_len, batch, causal != 0,
+                  page_size, num_cache_pages, num_heads, num_workers};
+  auto* h = new (std::nothrow) mla_schedule_s;
+  if (!h) return mla::fail(MLA_E_NOMEM, "host allocation failed");
+  mla_status st;
+  try {
+    st = mla::build_schedule(a, &h->s);
+  } catch (const std::bad_alloc&) {
+    st = mla::fail(MLA_E_NOMEM, "host allocation failed");
+  }
+  if (st != MLA_OK) {
+    delete h;
+    return st;
+  }
+  *out = h;
+  return MLA_OK;
+}
+
+void mla_schedule_sizes(mla_schedule_t s, int32_t* num_workers, int64_t* num_items,
+                        int64_t* num_merges, int64_t* num_slots) {
+  if (!s) return;
+  if (num_workers) *num_workers = s->s.num_workers;
+  if (num_items) *num_items = static_cast<int64_t>(s->s.items.size());
+  if (num_merges) *num_merges = static_cast<int64_t>(s->s.merges.size());
+  if (num_slots) *num_slots = s->s.num_slots;
+}
+
+void mla_schedule_copy(mla_schedule_t s, int32_t* worker_indptr, int32_t* items,
+                       int32_t* merges) {
+  if (!s) return;
+  if (worker_indptr)
+    std::memcpy(worker_indptr, s->s.worker_indptr.data(),
+                s->s.worker_indptr.size() * sizeof(int32_t));
+  if (items && !s->s.items.empty())
+    std::memcpy(items, s->s.items.data(), s->s.items.size() * sizeof(mla::WorkItem));
+  if (merges && !s->s.merges.empty())
+    std::memcpy(merges, s->s.merges.data(), s->s.merges.size() * sizeof(mla::MergeItem));
+}
+
+void mla_schedule_destroy(mla_schedule_t s) { delete s; }
+
+}  // extern "C"
