@@ -12,22 +12,31 @@
 //     items in order.  An item is one query token with ALL its heads, so a
 //     key tile staged in LDS is shared by every head of the token;
 //   * wave w owns heads [32w, 32w + 32); a workgroup has ceil(H / 32) waves;
-//   * keys are processed in tiles of 32, double-buffered in LDS: while the
-//     waves compute on one stage, the next tile is fetched into registers
-//     and then written to the other stage;
-//   * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16 with keys as M and heads as N,
-//     so each lane ends up holding 16 scores of ONE head and the softmax
-//     statistics are per lane (one cross-lane exchange per tile);
+//   * keys are processed in tiles of 32.  A tile is copied from HBM straight
+//     into LDS by global_load_lds (no staging registers), four tiles deep
+//     (4 x 36 KiB of the 160 KiB LDS), with explicit vmcnt waits and a bare
+//     s_barrier per tile;
+//   * one swizzled LDS layout serves both products: 16-byte chunk (key, dc)
+//     (dc = 8-column chunk of the 576 latent columns) sits at
+//     (dc/2)*1024 + (dc%2)*512 + (key ^ 4*(dc%2))*16, which the loader
+//     writes as 36 DMA instructions of 1 KiB and which keeps both read
+//     patterns free of bank conflicts;
+//   * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16 with keys as M and heads as N
+//     (K operand: ds_read_b128 of 32 keys x 16 B), so each lane ends up
+//     holding 16 scores of ONE head and the softmax statistics are per lane
+//     (one cross-lane exchange per tile);
 //   * O^T += V^T . P^T on the same MFMA with latent columns as M: the
-//     probabilities come straight from the score accumulators (no shuffle),
-//     and V^T is read from a transposed, swizzled copy of the tile's ckv
-//     columns that the loader writes beside the row-major K tile;
+//     probabilities come straight from the score accumulators, and the V^T
+//     operand is read from the same K tile with ds_read_b64_tr_b16, whose
+//     16-lane transpose turns four 8-byte row pieces into one column each;
 //   * softmax in base 2 against a per-head reference maximum fixed at the
 //     item's first tile: p = 2^(x - m_ref) is exact for any reference (output
 //     and LSE are normalised with the same value), so the O accumulators are
 //     never rescaled inside the key loop.  A later score more than 2^64 above
 //     the reference (which would overflow) makes the workgroup redo the item
 //     with the largest score seen as the reference;
+//   * page ids come through scalar loads, so no vector load inside the key
+//     loop ever forces the in-order vmcnt to drain the DMA queue;
 //   * items covering a token's whole key range write bf16 output + LSE;
 //     pieces of a split token write fp32 partials that a merge kernel combines.
 #include "kernels.h"
@@ -40,148 +49,168 @@ typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef short s16x4_t __attribute__((vector_size(8)));
+typedef short s16x8_t __attribute__((vector_size(16)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(4))) const int32_t const_i32_t;
 
 constexpr int kWave = 64;
-constexpr int kQChunks = kLatentDim / 16;          // 36 k-steps of 16 over 576
-constexpr int kKRowBytes = kLatentDim * 2 + 16;    // 1168 B: row pad spreads rows over banks
-constexpr int kKBytes = kTileKeys * kKRowBytes;    // 37376
-constexpr int kVtRowBytes = kTileKeys * 2;         // 64 B: one ckv column, 32 keys
-constexpr int kVtBytes = kLoraRank * kVtRowBytes;  // 32768
-constexpr int kStageBytes = kKBytes + kVtBytes;    // 70144
-constexpr int kStages = 2;
-constexpr int kFlagBytes = 16;                     // per-wave redo flags after the stages
-constexpr int kLoadUnits = 256;                    // (column chunk, key octet) pairs per tile
-constexpr float kMaxExponent = 64.0f;              // log2 headroom above the reference
+constexpr int kQChunks = kLatentDim / 16;         // 36 k-steps of 16 over 576
+constexpr int kDmaPerTile = kLatentDim / 16;      // 36 x 1 KiB (two 16-B chunks x 32 keys)
+constexpr int kTileBytes = kDmaPerTile * 1024;    // 36864
+constexpr int kStages = 4;
+constexpr int kFlagBytes = 16;                    // per-wave redo flags after the stages
+constexpr int kFinishRow = 128 + 4;               // floats per head row of the output staging
+constexpr int kFinishWaveBytes = (32 * kFinishRow + 32) * 4;  // per-wave staging + 1/l per head
+constexpr float kMaxExponent = 64.0f;             // log2 headroom above the reference
 constexpr float kLn2 = 0.693147180559945309f;
 
-// The transposed-V row of column c holds 4 chunks of 8 keys; chunk q is
-// stored at 16-byte slot q ^ vt_swizzle(c) so that the 8 (and 16) lanes that
-// read one chunk of consecutive columns, and the lanes that write 8
-// consecutive columns, fall into different LDS banks.
-__device__ __forceinline__ int vt_swizzle(int c) { return ((c >> 1) + (c >> 3)) & 3; }
-
-// Key of element i (0..7) of key octet (ks, half) inside a tile.  The P^T
-// operand of the P.V product takes score register j = 8 ks + i of lane
-// half `half`, which the 32x32 MFMA result layout places at key
-// 8 (j / 4) + 4 half + j % 4.
-__device__ __forceinline__ int octet_key(int ks, int half, int i) {
-  return 16 * ks + 8 * (i >> 2) + 4 * half + (i & 3);
-}
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector
+// memory operations are outstanding and leaves the other counters alone.
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
-struct TileRegs {
-  u32x4_t ckv[8];  // 8 keys x 16 B of one ckv column chunk
-  u32x4_t kpe;     // 16 B of one key's kpe
-};
+// Barrier without the memory fence of __syncthreads (which would wait for
+// every outstanding LDS DMA); the empty asm keeps the compiler from moving
+// LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 template <int NW>
 struct Attn {
-  static constexpr int NT = NW * kWave;
-  static constexpr int kRounds = (kLoadUnits + NT - 1) / NT;
+  static constexpr int kLoadsPerWave = (kDmaPerTile + NW - 1) / NW;
+  static constexpr int kWaitOne = kLoadsPerWave > 63 ? 63 : kLoadsPerWave;
+  static constexpr int kWaitTwo = 2 * kLoadsPerWave > 63 ? 63 : 2 * kLoadsPerWave;
 
   const AttnArgs& a;
   char* smem;
-  int tid, lane, l32, half, wave, head;
+  int lane, l32, half, wave, head;
   bool head_ok;
+  int ld_key, ld_off, qk_off, pv_off;  // per-lane LDS / row offsets
+  uint32_t lds_base;                   // LDS address of the stages
   // current item
   int token, kv_end, slot;
-  const int32_t* pages;  // the row's page ids
+  int page_base;  // index of the row's first page in kv_indices
 
   __device__ Attn(const AttnArgs& args, char* s) : a(args), smem(s) {
-    tid = threadIdx.x;
+    const int tid = threadIdx.x;
     lane = tid & 63;
     l32 = lane & 31;
     half = lane >> 5;
-    wave = tid >> 6;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     head = wave * 32 + l32;
     head_ok = head < a.num_heads;
+    lds_base = static_cast<uint32_t>(reinterpret_cast<size_t>((__attribute__((address_space(3))) char*)smem));
+    // loader: lane p fetches key (p%32) ^ 4(p/32), chunk parity p/32
+    ld_key = l32 ^ (4 * half);
+    ld_off = half * 16;
+    // score operand: key l32, chunk 2kk + half
+    qk_off = half * 512 + ((l32 ^ (4 * half)) * 16);
+    // P.V operand through the 16-lane transpose read: group G = lane/16 is
+    // (key half hf, 16-column group cg); source lane s of the group points at
+    // key 4hf + s/4 (+8 for the second read), columns 16cg + 4(s%4) .. +3.
+    const int G = lane >> 4, sl = lane & 15;
+    const int hf = G >> 1, cg = G & 1;
+    const int par = (sl >> 1) & 1;  // chunk parity of the source columns
+    const int key_l = 4 * hf + (sl >> 2);
+    pv_off = cg * 1024 + par * 512 + (sl & 1) * 8 + ((key_l ^ (4 * par)) * 16);
   }
 
-  __device__ __forceinline__ const uint16_t* key_row(int key) const {
+  // Page id of key `key` of the current row, for the lane's own key.  The
+  // page table is read with scalar loads only (wave-uniform addresses, made
+  // explicit with readfirstlane so no select is folded into a per-lane
+  // address): a vector load here would make the in-order vmcnt wait for every
+  // DMA in flight.
+  __device__ __forceinline__ int lane_page(int base, int key) const {
     const int P = a.page_size;
-    const int page = pages[key / P];
-    return a.kv_cache + (static_cast<int64_t>(page) * P + key % P) * kLatentDim;
+    const_i32_t* idx = (const_i32_t*)(a.kv_indices) + page_base;
+    const int first = base / P;
+    if (P % kTileKeys == 0)  // the whole tile is in one page
+      return __builtin_amdgcn_readfirstlane(idx[first]);
+    const int j = key / P - first;  // 0 .. 31
+    int v = __builtin_amdgcn_readfirstlane(idx[first]);
+#pragma unroll
+    for (int i = 1; i < kTileKeys; ++i) {
+      const int pi = __builtin_amdgcn_readfirstlane(idx[first + i]);
+      v = (j == i) ? pi : v;
+    }
+    return v;
   }
 
-  // Global -> registers for load round r of the tile starting at key `base`.
-  __device__ __forceinline__ void fetch(TileRegs& r, int base, int round) const {
-    const int u = tid + round * NT;
-    if (u >= kLoadUnits) return;
-    const int cc = u & 63, oct = u >> 6;
-    const int ks = oct >> 1, hf = oct & 1;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int key = base + octet_key(ks, hf, i);
-      r.ckv[i] = key < kv_end
-                     ? *reinterpret_cast<const u32x4_t*>(key_row(key) + cc * 8)
-                     : u32x4_t{0u, 0u, 0u, 0u};
-    }
-    const int kk = u >> 3, ch = u & 7;
-    const int key = base + kk;
-    r.kpe = key < kv_end ? *reinterpret_cast<const u32x4_t*>(key_row(key) + kLoraRank + ch * 8)
-                         : u32x4_t{0u, 0u, 0u, 0u};
+  // One 16-byte-per-lane DMA from global memory into LDS at lds_addr + 16 *
+  // lane.  Issued through asm so that the compiler, which cannot tell the
+  // stages apart, does not make later LDS reads wait for every DMA; the
+  // tile pipeline waits on vmcnt itself.  M0 holds the LDS base; one wait
+  // state separates its write from the DMA.
+  __device__ __forceinline__ static void dma16(const char* src, uint32_t lds_addr) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds_addr)
+                 : "memory", "m0");
   }
 
-  // Registers -> LDS stage: row-major K rows and the transposed V columns.
-  __device__ __forceinline__ void store(const TileRegs& r, char* stage, int round) const {
-    const int u = tid + round * NT;
-    if (u >= kLoadUnits) return;
-    const int cc = u & 63, oct = u >> 6;
-    const int ks = oct >> 1, hf = oct & 1;
-    char* K = stage;
-    char* VT = stage + kKBytes;
+  // DMA the 32-key tile starting at key `base` into LDS stage `stage`.  Keys
+  // beyond the item's range re-read its last key (finite data, masked later).
+  __device__ __forceinline__ void issue_tile(int base, int stage) const {
+    int key = base + ld_key;
+    key = key < kv_end ? key : kv_end - 1;
+    const int P = a.page_size;
+    const int page = lane_page(base, key);
+    const char* src = reinterpret_cast<const char*>(
+        a.kv_cache + (static_cast<int64_t>(page) * P + key % P) * kLatentDim) + ld_off;
+    const uint32_t dst = lds_base + stage * kTileBytes;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      *reinterpret_cast<u32x4_t*>(K + octet_key(ks, hf, i) * kKRowBytes + cc * 16) = r.ckv[i];
+    for (int j = 0; j < kLoadsPerWave; ++j) {
+      const int I = wave + j * NW;
+      if (NW * kLoadsPerWave == kDmaPerTile || I < kDmaPerTile) dma16(src + I * 32, dst + I * 1024);
     }
-    const int kk = u >> 3, ch = u & 7;
-    *reinterpret_cast<u32x4_t*>(K + kk * kKRowBytes + kLoraRank * 2 + ch * 16) = r.kpe;
-    // 8x8 transpose: column e of the 8 key chunks -> 8 keys of column 8cc+e.
-    const int q = 2 * ks + hf;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      u32x4_t w;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const unsigned lo = r.ckv[2 * j][e >> 1];
-        const unsigned hi = r.ckv[2 * j + 1][e >> 1];
-        w[j] = (e & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-      }
-      const int c = cc * 8 + e;
-      *reinterpret_cast<u32x4_t*>(VT + c * kVtRowBytes + ((q ^ vt_swizzle(c)) * 16)) = w;
-    }
+  }
+
+  // Wait until this wave's DMAs for the tile `later` tiles before the newest
+  // have landed.
+  __device__ __forceinline__ void wait_tile(int later) const {
+    if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kWaitTwo));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kWaitOne));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   }
 
   __device__ void run() {
-    const int w_begin = a.worker_indptr[blockIdx.x];
-    const int w_end = a.worker_indptr[blockIdx.x + 1];
+    const_i32_t* widx = (const_i32_t*)(a.worker_indptr);
+    const int w_begin = widx[blockIdx.x];
+    const int w_end = widx[blockIdx.x + 1];
     const int H = a.num_heads;
 
     for (int it = w_begin; it < w_end; ++it) {
-      const WorkItem item = a.items[it];
-      token = item.token;
-      kv_end = item.kv_end;
-      slot = item.slot;
-      pages = a.kv_indices + a.kv_indptr[item.row];
-      const int kv_begin = item.kv_begin;
+      const_i32_t* item = (const_i32_t*)(a.items) + it * 8;  // WorkItem fields
+      token = item[0];
+      const int row = item[1];
+      const int kv_begin = item[2];
+      kv_end = item[3];
+      slot = item[4];
+      page_base = ((const_i32_t*)(a.kv_indptr))[row];
 
       // Query of this lane's head: 36 chunks of 8 along the 576 latent dims,
       // element layout matching the K operand (dims 16 kk + 8 half + i).
       bf16x8_t q[kQChunks];
       {
-        const uint16_t* qn = a.q_nope + (static_cast<int64_t>(token) * H + head) * kLoraRank;
-        const uint16_t* qp = a.q_pe + (static_cast<int64_t>(token) * H + head) * kRopeDim;
+        // Lanes of padding heads read head 0's row and zero it.
+        const int hq = head_ok ? head : 0;
+        const uint16_t* qn = a.q_nope + (static_cast<int64_t>(token) * H + hq) * kLoraRank;
+        const uint16_t* qp = a.q_pe + (static_cast<int64_t>(token) * H + hq) * kRopeDim;
+        const unsigned keep = head_ok ? 0xFFFFFFFFu : 0u;
 #pragma unroll
         for (int kk = 0; kk < kQChunks; ++kk) {
-          u32x4_t v = {0u, 0u, 0u, 0u};
-          if (head_ok) {
-            v = kk < kLoraRank / 16
-                    ? *reinterpret_cast<const u32x4_t*>(qn + kk * 16 + half * 8)
-                    : *reinterpret_cast<const u32x4_t*>(qp + (kk - kLoraRank / 16) * 16 + half * 8);
-          }
+          u32x4_t v = kk < kLoraRank / 16
+                          ? *reinterpret_cast<const u32x4_t*>(qn + kk * 16 + half * 8)
+                          : *reinterpret_cast<const u32x4_t*>(qp + (kk - kLoraRank / 16) * 16 + half * 8);
+          v &= keep;
           q[kk] = __builtin_bit_cast(bf16x8_t, v);
         }
       }
@@ -198,30 +227,25 @@ struct Attn {
           for (int j = 0; j < 16; ++j) o[mb][j] = 0.f;
         l_run = 0.f;
         if (ntiles == 0) break;
-        TileRegs regs;
-        for (int r = 0; r < kRounds; ++r) {
-          fetch(regs, kv_begin, r);
-          store(regs, smem, r);
-        }
+        // Every wave is done with the previous item's output staging (LDS),
+        // and this wave's query loads and earlier stores retire before the
+        // DMA queue is counted tile by tile.
         __syncthreads();
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        asm volatile("" ::: "memory");
+        for (int t = 0; t < kStages - 1 && t < ntiles; ++t)
+          issue_tile(kv_begin + t * kTileKeys, t);
         for (int t = 0; t < ntiles; ++t) {
-          const int base = kv_begin + t * kTileKeys;
-          const bool more = t + 1 < ntiles;
-          if (more) fetch(regs, base + kTileKeys, 0);
-          char* stage = smem + (t & 1) * kStageBytes;
-          compute_tile(stage, base, q, o, m_ref, m_seen, l_run);
-          if (more) {
-            char* next = smem + ((t + 1) & 1) * kStageBytes;
-            store(regs, next, 0);
-            for (int r = 1; r < kRounds; ++r) {
-              fetch(regs, base + kTileKeys, r);
-              store(regs, next, r);
-            }
-          }
-          __syncthreads();
+          const int issued_after = ntiles - 1 - t < kStages - 2 ? ntiles - 1 - t : kStages - 2;
+          wait_tile(issued_after);
+          lds_barrier();
+          if (t + kStages - 1 < ntiles)
+            issue_tile(kv_begin + (t + kStages - 1) * kTileKeys, (t + kStages - 1) % kStages);
+          compute_tile(smem + (t % kStages) * kTileBytes, kv_begin + t * kTileKeys, q, o, m_ref,
+                       m_seen, l_run);
         }
         // Redo the item if any head of the workgroup overflowed its reference.
-        int* flags = reinterpret_cast<int*>(smem + kStages * kStageBytes);
+        int* flags = reinterpret_cast<int*>(smem + kStages * kTileBytes);
         const bool redo = __any(m_seen > m_ref + kMaxExponent);
         if (lane == 0) flags[wave] = redo ? 1 : 0;
         __syncthreads();
@@ -232,26 +256,39 @@ struct Attn {
         if (!any_redo) break;
         m_ref = m_seen;
       }
-      const float m_run = m_ref;
-      finish(o, m_run, l_run);
+      finish(o, m_ref, l_run);
     }
   }
 
-  __device__ __forceinline__ void compute_tile(const char* stage, int base,
+  __device__ __forceinline__ void compute_tile(const char* K, int base,
                                                const bf16x8_t (&q)[kQChunks],
                                                f32x16_t (&o)[kLoraRank / 32], float& m_ref,
                                                float& m_seen, float& l_run) const {
-    const char* K = stage;
-    const char* VT = stage + kKBytes;
     // S^T[key, head] over the 576 latent dims.
     f32x16_t s;
 #pragma unroll
     for (int j = 0; j < 16; ++j) s[j] = 0.f;
-    const char* krow = K + l32 * kKRowBytes + half * 16;
+    // Operands are read kAhead k-steps before their MFMA, so LDS latency
+    // overlaps the MFMA pipeline.
+    const char* kq = K + qk_off;
+    constexpr int kAhead = 3;
+    bf16x8_t kbuf[kAhead];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) kbuf[i] = *reinterpret_cast<const bf16x8_t*>(kq + i * 1024);
 #pragma unroll
     for (int kk = 0; kk < kQChunks; ++kk) {
-      const bf16x8_t kv = *reinterpret_cast<const bf16x8_t*>(krow + kk * 32);
+      const bf16x8_t kv = kbuf[kk % kAhead];
+      if (kk + kAhead < kQChunks)
+        kbuf[kk % kAhead] = *reinterpret_cast<const bf16x8_t*>(kq + (kk + kAhead) * 1024);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, q[kk], s, 0, 0, 0);
+    }
+    // Keep the reads kAhead steps ahead: the scheduler would otherwise pull
+    // each read down next to its MFMA.
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);  // DS reads
+#pragma unroll
+    for (int kk = 0; kk < kQChunks; ++kk) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      if (kk + kAhead < kQChunks) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
     }
     // Scale to base 2, mask keys beyond the item's range, tile max.
     float x[16];
@@ -274,55 +311,92 @@ struct Attn {
       p[j >> 3][j & 7] = static_cast<__bf16>(e);
     }
     // O^T[col, head] += V^T[col, key] . P^T[key, head].
+    const char* kv = K + pv_off;
+    auto vload = [&](int step) {
+      const char* ptr = kv + (step >> 1) * 2048 + (step & 1) * 256;
+      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(ptr));
+      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(ptr + 128));
+      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    constexpr int kSteps = 2 * (kLoraRank / 32);  // (column block, key half) pairs
+    bf16x8_t vbuf[kAhead];
 #pragma unroll
-    for (int mb = 0; mb < kLoraRank / 32; ++mb) {
-      const int c = mb * 32 + l32;
-      const char* vrow = VT + c * kVtRowBytes;
-      const int sw = vt_swizzle(c);
+    for (int i = 0; i < kAhead; ++i) vbuf[i] = vload(i);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(vrow + (((2 * ks + half) ^ sw) * 16));
-        o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, p[ks], o[mb], 0, 0, 0);
-      }
+    for (int st = 0; st < kSteps; ++st) {
+      const bf16x8_t v = vbuf[st % kAhead];
+      if (st + kAhead < kSteps) vbuf[st % kAhead] = vload(st + kAhead);
+      o[st >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, p[st & 1], o[st >> 1], 0, 0, 0);
     }
   }
 
+  // Writes the item's result.  The accumulators are never touched by VALU
+  // code here (that makes the compiler shuttle all 256 of them through
+  // VGPRs): a partial piece stores the raw sums and 1/l for the merge kernel;
+  // a final item stages the raw sums through this wave's LDS region, then
+  // normalises, converts and stores 16 bytes per lane, 4 heads x 256 B
+  // contiguous per instruction.  The caller has made the LDS stages free.
   __device__ __forceinline__ void finish(f32x16_t (&o)[kLoraRank / 32], float m_run,
                                          float l_run) const {
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const bool any = l_tot > 0.f;
     const float inv = any ? 1.f / l_tot : 0.f;
     const float lse_v = any ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
-    if (!head_ok) return;
     const int H = a.num_heads;
-    if (slot < 0) {
-      uint16_t* dst = a.out + (static_cast<int64_t>(token) * H + head) * kLoraRank;
+    if (slot >= 0) {
+      if (head_ok) {
+        float* dst = a.part_o + (static_cast<int64_t>(slot) * H + head) * kLoraRank;
 #pragma unroll
-      for (int mb = 0; mb < kLoraRank / 32; ++mb)
+        for (int mb = 0; mb < kLoraRank / 32; ++mb)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4_t w = {o[mb][4 * q4], o[mb][4 * q4 + 1], o[mb][4 * q4 + 2],
+                               o[mb][4 * q4 + 3]};
+            *reinterpret_cast<f32x4_t*>(dst + mb * 32 + q4 * 8 + half * 4) = w;
+          }
+        if (half == 0) {
+          const int64_t sh = static_cast<int64_t>(slot) * H + head;
+          a.part_lse[sh] = lse_v;
+          a.part_scale[sh] = inv;
+        }
+      }
+      return;
+    }
+    float* R = reinterpret_cast<float*>(smem + wave * kFinishWaveBytes);
+    float* inv_h = R + 32 * kFinishRow;
+    if (half == 0) inv_h[l32] = inv;
+    if (a.lse && head_ok && half == 0) a.lse[static_cast<int64_t>(token) * H + head] = lse_v;
+#pragma unroll
+    for (int round = 0; round < kLoraRank / 128; ++round) {
+#pragma unroll
+      for (int m4 = 0; m4 < 4; ++m4) {
+        const int mb = round * 4 + m4;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const int c = mb * 32 + q4 * 8 + half * 4;
-          u32x2_t w;
-          w[0] = f32_to_bf16_bits(o[mb][4 * q4 + 0] * inv) |
-                 (static_cast<unsigned>(f32_to_bf16_bits(o[mb][4 * q4 + 1] * inv)) << 16);
-          w[1] = f32_to_bf16_bits(o[mb][4 * q4 + 2] * inv) |
-                 (static_cast<unsigned>(f32_to_bf16_bits(o[mb][4 * q4 + 3] * inv)) << 16);
-          *reinterpret_cast<u32x2_t*>(dst + c) = w;
+          const f32x4_t w = {o[mb][4 * q4], o[mb][4 * q4 + 1], o[mb][4 * q4 + 2],
+                             o[mb][4 * q4 + 3]};
+          *reinterpret_cast<f32x4_t*>(R + l32 * kFinishRow + m4 * 32 + q4 * 8 + half * 4) = w;
         }
-      if (a.lse && half == 0) a.lse[static_cast<int64_t>(token) * H + head] = lse_v;
-    } else {
-      float* dst = a.part_o + (static_cast<int64_t>(slot) * H + head) * kLoraRank;
+      }
+      // lane: head h = (lane + 64 r) / 16 of the wave, 8 columns cc * 8 of
+      // this round's 128.
 #pragma unroll
-      for (int mb = 0; mb < kLoraRank / 32; ++mb)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int c = mb * 32 + q4 * 8 + half * 4;
-          f32x4_t w;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) w[i] = o[mb][4 * q4 + i] * inv;
-          *reinterpret_cast<f32x4_t*>(dst + c) = w;
-        }
-      if (half == 0) a.part_lse[static_cast<int64_t>(slot) * H + head] = lse_v;
+      for (int r = 0; r < 8; ++r) {
+        const int qi = lane + 64 * r;
+        const int h = qi >> 4, cc = qi & 15;
+        const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(R + h * kFinishRow + cc * 8);
+        const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(R + h * kFinishRow + cc * 8 + 4);
+        const float sc = inv_h[h];
+        u32x4_t w;
+        w[0] = f32_to_bf16_bits(v0[0] * sc) | (static_cast<unsigned>(f32_to_bf16_bits(v0[1] * sc)) << 16);
+        w[1] = f32_to_bf16_bits(v0[2] * sc) | (static_cast<unsigned>(f32_to_bf16_bits(v0[3] * sc)) << 16);
+        w[2] = f32_to_bf16_bits(v1[0] * sc) | (static_cast<unsigned>(f32_to_bf16_bits(v1[1] * sc)) << 16);
+        w[3] = f32_to_bf16_bits(v1[2] * sc) | (static_cast<unsigned>(f32_to_bf16_bits(v1[3] * sc)) << 16);
+        const int hg = wave * 32 + h;
+        if (hg < H)
+          *reinterpret_cast<u32x4_t*>(a.out + (static_cast<int64_t>(token) * H + hg) * kLoraRank +
+                                      round * 128 + cc * 8) = w;
+      }
     }
   }
 };
@@ -330,7 +404,7 @@ struct Attn {
 template <int NW>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attention_kernel(AttnArgs args) {
-  __shared__ __attribute__((aligned(16))) char smem[kStages * kStageBytes + kFlagBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * kTileBytes + kFlagBytes];
   Attn<NW> k(args, smem);
   k.run();
 }

@@ -68,7 +68,8 @@ struct mla_plan_s {
   size_t d_stage_cap = 0;
   size_t off_items = 0, off_merges = 0, off_kv_indptr = 0, off_kv_indices = 0;
 
-  // Split-KV partials: fp32 o [slots, H, 512] then lse [slots, H].
+  // Split-KV partials: fp32 raw o [slots, H, 512], then lse [slots, H], then
+  // 1/l [slots, H].
   float* d_part = nullptr;
   size_t part_cap = 0;  // floats
 
@@ -139,12 +140,15 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
   const size_t n_items = s.items.size() * sizeof(mla::WorkItem);
   const size_t n_merges = s.merges.size() * sizeof(mla::MergeItem);
   const size_t n_kvp = static_cast<size_t>(s.batch + 1) * sizeof(int32_t);
+  // kv_indices plus 32 spare entries: the kernel reads the page ids of a
+  // 32-key tile as one scalar block that may run past a row's last page.
   const size_t n_idx = static_cast<size_t>(s.nnz) * sizeof(int32_t);
+  const size_t n_idx_pad = n_idx + mla::kTileKeys * sizeof(int32_t);
   const size_t off_items = align_up(n_wi);
   const size_t off_merges = off_items + align_up(n_items);
   const size_t off_kvp = off_merges + align_up(n_merges);
   const size_t off_idx = off_kvp + align_up(n_kvp);
-  const size_t total = off_idx + align_up(n_idx);
+  const size_t total = off_idx + align_up(n_idx_pad);
 
   // The previous copy must have read the staging buffer before we refill it.
   hipError_t e;
@@ -162,7 +166,7 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
     p->h_stage_cap = total;
   }
   const size_t part_floats =
-      static_cast<size_t>(s.num_slots) * p->num_heads * (mla::kLoraRank + 1);
+      static_cast<size_t>(s.num_slots) * p->num_heads * (mla::kLoraRank + 2);
   if (total > p->d_stage_cap || part_floats > p->part_cap) {
     // Buffers may still be read by enqueued kernels of an earlier plan.
     e = hipDeviceSynchronize();
@@ -189,6 +193,7 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
   if (n_merges) std::memcpy(p->h_stage + off_merges, s.merges.data(), n_merges);
   if (s.batch > 0) std::memcpy(p->h_stage + off_kvp, kv_indptr, n_kvp);
   if (n_idx) std::memcpy(p->h_stage + off_idx, kv_indices, n_idx);
+  std::memset(p->h_stage + off_idx + n_idx, 0, n_idx_pad - n_idx);
   e = hipMemcpyAsync(p->d_stage, p->h_stage, total, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
   e = hipEventRecord(p->h2d_done, stream);
@@ -227,6 +232,7 @@ mla_status mla_run(mla_plan_t p, const void* q_nope, const void* q_pe, const voi
   a.lse = lse;
   a.part_o = p->d_part;
   a.part_lse = p->d_part ? p->d_part + slots_h * mla::kLoraRank : nullptr;
+  a.part_scale = p->d_part ? a.part_lse + slots_h : nullptr;
   a.worker_indptr = reinterpret_cast<const int32_t*>(p->d_stage);
   a.items = reinterpret_cast<const mla::WorkItem*>(p->d_stage + p->off_items);
   a.kv_indptr = reinterpret_cast<const int32_t*>(p->d_stage + p->off_kv_indptr);
@@ -240,6 +246,7 @@ mla_status mla_run(mla_plan_t p, const void* q_nope, const void* q_pe, const voi
     mla::SplitMergeArgs m{};
     m.part_o = a.part_o;
     m.part_lse = a.part_lse;
+    m.part_scale = a.part_scale;
     m.merges = reinterpret_cast<const mla::MergeItem*>(p->d_stage + p->off_merges);
     m.out = a.out;
     m.lse = lse;
