@@ -18,17 +18,21 @@
 //     s_barrier per tile;
 //   * one swizzled LDS layout serves both products: 16-byte chunk (key, dc)
 //     (dc = 8-column chunk of the 576 latent columns) sits at
-//     (dc/2)*1024 + (dc%2)*512 + (key ^ 4*(dc%2))*16, which the loader
-//     writes as 36 DMA instructions of 1 KiB and which keeps both read
-//     patterns free of bank conflicts;
-//   * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16 with keys as M and heads as N
-//     (K operand: ds_read_b128 of 32 keys x 16 B), so each lane ends up
-//     holding 16 scores of ONE head and the softmax statistics are per lane
-//     (one cross-lane exchange per tile);
-//   * O^T += V^T . P^T on the same MFMA with latent columns as M: the
-//     probabilities come straight from the score accumulators, and the V^T
-//     operand is read from the same K tile with ds_read_b64_tr_b16, whose
-//     16-lane transpose turns four 8-byte row pieces into one column each;
+//     (dc/2)*1024 + (dc%2)*512 + (key ^ 4*(dc%2) ^ 8*((dc/2)%2))*16, which
+//     the loader writes as 36 DMA instructions of 1 KiB and which keeps both
+//     read patterns free of bank conflicts on the 64-bank LDS (16 lanes per
+//     pass for 16-byte reads, 32 lanes for 8-byte reads);
+//   * S^T = K . Q^T on v_mfma_f32_16x16x32_bf16: four independent
+//     accumulator chains (2 key blocks x 2 head blocks of 16), so the 18
+//     k-steps never wait on a previous MFMA's result.  One exchange of half
+//     the scores with lane^16 then leaves each lane with 16 scores of ONE
+//     head (lane l: head l%32, keys 16ks + 8(l/32) + e), so the softmax
+//     statistics are per lane plus one cross-lane max per tile;
+//   * O^T += V^T . P^T on v_mfma_f32_32x32x16_bf16 with latent columns as M
+//     and heads as N: the probabilities are the B operand as they stand, and
+//     the V^T operand is read from the same K tile with ds_read_b64_tr_b16,
+//     whose 16-lane transpose turns four 8-byte row pieces into one column
+//     each.  The 16 column blocks are independent accumulators;
 //   * softmax in base 2 against a per-head reference maximum fixed at the
 //     item's first tile: p = 2^(x - m_ref) is exact for any reference (output
 //     and LSE are normalised with the same value), so the O accumulators are
@@ -56,11 +60,12 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(4))) const int32_t const_i32_t;
 
 constexpr int kWave = 64;
-constexpr int kQChunks = kLatentDim / 16;         // 36 k-steps of 16 over 576
+constexpr int kQSteps = kLatentDim / 32;          // 18 k-steps of 32 over 576
 constexpr int kDmaPerTile = kLatentDim / 16;      // 36 x 1 KiB (two 16-B chunks x 32 keys)
 constexpr int kTileBytes = kDmaPerTile * 1024;    // 36864
 constexpr int kStages = 4;
 constexpr int kFlagBytes = 16;                    // per-wave redo flags after the stages
+constexpr int kMaxItemPages = 1024;               // page ids staged per item (tile-aligned pages)
 constexpr int kFinishRow = 128 + 4;               // floats per head row of the output staging
 constexpr int kFinishWaveBytes = (32 * kFinishRow + 32) * 4;  // per-wave staging + 1/l per head
 constexpr float kMaxExponent = 64.0f;             // log2 headroom above the reference
@@ -83,7 +88,7 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int NW>
+template <int NW, bool kTileInPage>
 struct Attn {
   static constexpr int kLoadsPerWave = (kDmaPerTile + NW - 1) / NW;
   static constexpr int kWaitOne = kLoadsPerWave > 63 ? 63 : kLoadsPerWave;
@@ -93,11 +98,12 @@ struct Attn {
   char* smem;
   int lane, l32, half, wave, head;
   bool head_ok;
-  int ld_key, ld_off, qk_off, pv_off;  // per-lane LDS / row offsets
+  int ld_key, ld_off, qk_off, pv_off0, pv_off1;  // per-lane LDS / row offsets
   uint32_t lds_base;                   // LDS address of the stages
   // current item
   int token, kv_end, slot;
-  int page_base;  // index of the row's first page in kv_indices
+  int page_base;   // index of the row's first page in kv_indices
+  int first_page;  // row page index of the item's first key (tile-aligned pages)
 
   __device__ Attn(const AttnArgs& args, char* s) : a(args), smem(s) {
     const int tid = threadIdx.x;
@@ -108,19 +114,27 @@ struct Attn {
     head = wave * 32 + l32;
     head_ok = head < a.num_heads;
     lds_base = static_cast<uint32_t>(reinterpret_cast<size_t>((__attribute__((address_space(3))) char*)smem));
-    // loader: lane p fetches key (p%32) ^ 4(p/32), chunk parity p/32
+    // loader: lane p of DMA instruction I fetches key (p%32) ^ 4(p/32) ^ 8(I%2),
+    // chunk 2I + p/32 (the XOR by 8 is folded in when the DMA is issued)
     ld_key = l32 ^ (4 * half);
     ld_off = half * 16;
-    // score operand: key l32, chunk 2kk + half
-    qk_off = half * 512 + ((l32 ^ (4 * half)) * 16);
+    // score operand (16x16x32, A = K): lane (l16 = key in a 16-key block,
+    // g4 = lane/16) reads chunk 4ks + g4 of key 16kb + l16 at
+    // ks*2048 + kb*256 + qk_off
+    {
+      const int l16 = lane & 15, g4 = lane >> 4;
+      qk_off = (g4 >> 1) * 1024 + (g4 & 1) * 512 +
+               ((l16 ^ (4 * (g4 & 1)) ^ (8 * ((g4 >> 1) & 1))) * 16);
+    }
     // P.V operand through the 16-lane transpose read: group G = lane/16 is
-    // (key half hf, 16-column group cg); source lane s of the group points at
-    // key 4hf + s/4 (+8 for the second read), columns 16cg + 4(s%4) .. +3.
+    // (key half g2, 16-column group cg); source lane s of the group points at
+    // key 16ks + 8g2 + 4r + s/4 for read r (0, 1), columns 16cg + 4(s%4) .. +3.
     const int G = lane >> 4, sl = lane & 15;
-    const int hf = G >> 1, cg = G & 1;
+    const int g2 = G >> 1, cg = G & 1;
     const int par = (sl >> 1) & 1;  // chunk parity of the source columns
-    const int key_l = 4 * hf + (sl >> 2);
-    pv_off = cg * 1024 + par * 512 + (sl & 1) * 8 + ((key_l ^ (4 * par)) * 16);
+    const int pv_base = cg * 1024 + par * 512 + (sl & 1) * 8;
+    pv_off0 = pv_base + ((8 * (g2 ^ cg) + 4 * (0 ^ par) + (sl >> 2)) * 16);
+    pv_off1 = pv_base + ((8 * (g2 ^ cg) + 4 * (1 ^ par) + (sl >> 2)) * 16);
   }
 
   // Page id of key `key` of the current row, for the lane's own key.  The
@@ -132,7 +146,7 @@ struct Attn {
     const int P = a.page_size;
     const_i32_t* idx = (const_i32_t*)(a.kv_indices) + page_base;
     const int first = base / P;
-    if (P % kTileKeys == 0)  // the whole tile is in one page
+    if (kTileInPage)  // page_size % 32 == 0: the whole tile is in one page
       return __builtin_amdgcn_readfirstlane(idx[first]);
     const int j = key / P - first;  // 0 .. 31
     int v = __builtin_amdgcn_readfirstlane(idx[first]);
@@ -148,29 +162,88 @@ struct Attn {
   // lane.  Issued through asm so that the compiler, which cannot tell the
   // stages apart, does not make later LDS reads wait for every DMA; the
   // tile pipeline waits on vmcnt itself.  M0 holds the LDS base; one wait
-  // state separates its write from the DMA.
+  // state separates its write from the DMA.  Volatile asm keeps its order
+  // against the barriers (also volatile asm); the stage it writes is not
+  // read before the next barrier.
   __device__ __forceinline__ static void dma16(const char* src, uint32_t lds_addr) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :
-                 : "v"(src), "s"(lds_addr)
-                 : "memory", "m0");
+                 : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+                 : "m0");
   }
 
-  // DMA the 32-key tile starting at key `base` into LDS stage `stage`.  Keys
-  // beyond the item's range re-read its last key (finite data, masked later).
-  __device__ __forceinline__ void issue_tile(int base, int stage) const {
-    int key = base + ld_key;
-    key = key < kv_end ? key : kv_end - 1;
+  // The same DMA with a uniform 64-bit base (SGPR pair) and a 32-bit lane
+  // offset, for tiles that lie in one page.
+  // Both uniform operands pass through readfirstlane so that they are SGPRs
+  // even where the compiler cannot prove them uniform.
+  __device__ __forceinline__ static void dma16s(uint32_t voff, const char* sbase,
+                                                uint32_t lds_addr) {
+    const uint64_t b = reinterpret_cast<uint64_t>(sbase);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32));
+    const uint64_t sb = (static_cast<uint64_t>(hi) << 32) | lo;
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sb), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+                 : "m0");
+  }
+
+  // Source rows and LDS destination of one tile's DMAs for this lane: even
+  // DMA instructions fetch key ld_key, odd ones key ld_key ^ 8.  Keys beyond
+  // the item's range re-read its last key (finite data, masked later).
+  struct TileDma {
+    const char* src_e;  // general pages: per-lane row addresses
+    const char* src_o;
+    const char* sbase;  // tile in one page: page base (uniform) ...
+    uint32_t voff_e;    // ... and the row offsets of the even / odd DMAs' key
+    uint32_t voff_o;
+    uint32_t dst;
+  };
+
+  __device__ __forceinline__ TileDma prep_tile(int base, int stage) const {
     const int P = a.page_size;
-    const int page = lane_page(base, key);
-    const char* src = reinterpret_cast<const char*>(
-        a.kv_cache + (static_cast<int64_t>(page) * P + key % P) * kLatentDim) + ld_off;
-    const uint32_t dst = lds_base + stage * kTileBytes;
-#pragma unroll
-    for (int j = 0; j < kLoadsPerWave; ++j) {
-      const int I = wave + j * NW;
-      if (NW * kLoadsPerWave == kDmaPerTile || I < kDmaPerTile) dma16(src + I * 32, dst + I * 1024);
+    int ke = base + ld_key, ko = base + (ld_key ^ 8);
+    ke = ke < kv_end ? ke : kv_end - 1;
+    ko = ko < kv_end ? ko : kv_end - 1;
+    TileDma d;
+    d.dst = lds_base + stage * kTileBytes;
+    if (kTileInPage) {  // one page id per tile, staged in LDS for the item
+      const int pg = __builtin_amdgcn_readfirstlane(page_lds()[base / P - first_page]);
+      d.sbase = reinterpret_cast<const char*>(a.kv_cache + static_cast<int64_t>(pg) * P * kLatentDim);
+      d.voff_e = static_cast<uint32_t>((ke % P) * (kLatentDim * 2) + ld_off);
+      d.voff_o = static_cast<uint32_t>((ko % P) * (kLatentDim * 2) + ld_off);
+      d.src_e = d.src_o = nullptr;
+    } else {
+      const int pe = lane_page(base, ke), po = lane_page(base, ko);
+      d.src_e = reinterpret_cast<const char*>(
+          a.kv_cache + (static_cast<int64_t>(pe) * P + ke % P) * kLatentDim) + ld_off;
+      d.src_o = reinterpret_cast<const char*>(
+          a.kv_cache + (static_cast<int64_t>(po) * P + ko % P) * kLatentDim) + ld_off;
+      d.sbase = nullptr;
+      d.voff_e = d.voff_o = 0;
     }
+    return d;
+  }
+
+  // DMA instruction j (0 .. kLoadsPerWave-1) of this wave for a tile.
+  __device__ __forceinline__ void issue_one(const TileDma& d, int j) const {
+    const int I = wave + j * NW;
+    if (NW * kLoadsPerWave == kDmaPerTile || I < kDmaPerTile) {
+      if (kTileInPage)  // (with an even number of waves I has this wave's parity)
+        dma16s(((I & 1) ? d.voff_o : d.voff_e) + I * 32, d.sbase, d.dst + I * 1024);
+      else
+        dma16(((I & 1) ? d.src_o : d.src_e) + I * 32, d.dst + I * 1024);
+    }
+  }
+
+  __device__ __forceinline__ void issue_tile(int base, int stage) const {
+    const TileDma d = prep_tile(base, stage);
+#pragma unroll
+    for (int j = 0; j < kLoadsPerWave; ++j) issue_one(d, j);
+  }
+
+  __device__ __forceinline__ int* page_lds() const {
+    return reinterpret_cast<int*>(smem + kStages * kTileBytes + kFlagBytes);
   }
 
   // Wait until this wave's DMAs for the tile `later` tiles before the newest
@@ -196,22 +269,26 @@ struct Attn {
       slot = item[4];
       page_base = ((const_i32_t*)(a.kv_indptr))[row];
 
-      // Query of this lane's head: 36 chunks of 8 along the 576 latent dims,
-      // element layout matching the K operand (dims 16 kk + 8 half + i).
-      bf16x8_t q[kQChunks];
-      {
-        // Lanes of padding heads read head 0's row and zero it.
-        const int hq = head_ok ? head : 0;
+      // Query as the B operand of the 16x16x32 score MFMAs: for head block
+      // hb, lane (l16, g4) holds head 32 wave + 16 hb + l16, dims
+      // 32 ks + 8 g4 .. +8.  Padding heads read head 0's row and zero it.
+      bf16x8_t q[2][kQSteps];
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const int h = wave * 32 + hb * 16 + (lane & 15);
+        const bool ok = h < H;
+        const int hq = ok ? h : 0;
         const uint16_t* qn = a.q_nope + (static_cast<int64_t>(token) * H + hq) * kLoraRank;
         const uint16_t* qp = a.q_pe + (static_cast<int64_t>(token) * H + hq) * kRopeDim;
-        const unsigned keep = head_ok ? 0xFFFFFFFFu : 0u;
+        const unsigned keep = ok ? 0xFFFFFFFFu : 0u;
+        const int dl = 8 * (lane >> 4);
 #pragma unroll
-        for (int kk = 0; kk < kQChunks; ++kk) {
-          u32x4_t v = kk < kLoraRank / 16
-                          ? *reinterpret_cast<const u32x4_t*>(qn + kk * 16 + half * 8)
-                          : *reinterpret_cast<const u32x4_t*>(qp + (kk - kLoraRank / 16) * 16 + half * 8);
+        for (int ks = 0; ks < kQSteps; ++ks) {
+          u32x4_t v = ks < kLoraRank / 32
+                          ? *reinterpret_cast<const u32x4_t*>(qn + ks * 32 + dl)
+                          : *reinterpret_cast<const u32x4_t*>(qp + (ks - kLoraRank / 32) * 32 + dl);
           v &= keep;
-          q[kk] = __builtin_bit_cast(bf16x8_t, v);
+          q[hb][ks] = __builtin_bit_cast(bf16x8_t, v);
         }
       }
 
@@ -227,22 +304,50 @@ struct Attn {
           for (int j = 0; j < 16; ++j) o[mb][j] = 0.f;
         l_run = 0.f;
         if (ntiles == 0) break;
-        // Every wave is done with the previous item's output staging (LDS),
-        // and this wave's query loads and earlier stores retire before the
-        // DMA queue is counted tile by tile.
+        // Every wave is done with the previous item's output staging and
+        // page ids (LDS); then this item's page ids are staged, and this
+        // wave's query loads and earlier stores retire before the DMA queue
+        // is counted tile by tile.
         __syncthreads();
+        if (kTileInPage) {
+          const int P = a.page_size;
+          first_page = kv_begin / P;
+          const int n = (kv_end - 1) / P - first_page + 1;  // <= kMaxItemPages
+          for (int i = threadIdx.x; i < n; i += NW * kWave)
+            page_lds()[i] = a.kv_indices[page_base + first_page + i];
+          __syncthreads();
+        }
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         asm volatile("" ::: "memory");
-        for (int t = 0; t < kStages - 1 && t < ntiles; ++t)
-          issue_tile(kv_begin + t * kTileKeys, t);
-        for (int t = 0; t < ntiles; ++t) {
-          const int issued_after = ntiles - 1 - t < kStages - 2 ? ntiles - 1 - t : kStages - 2;
-          wait_tile(issued_after);
+#pragma unroll
+        for (int t = 0; t < kStages - 1; ++t)
+          if (t < ntiles) issue_tile(kv_begin + t * kTileKeys, t);
+        bf16x8_t p[2];
+        // Steady state (straight-line body): tile t has kStages-2 later
+        // tiles in flight; tile t+3 is issued into the stage tile t-1 used.
+        const int steady = ntiles - (kStages - 1);
+        int t = 0;
+        for (; t < steady; ++t) {
+          wait_tile(kStages - 2);  // tile t has landed ...
+          lds_barrier();           // ... for every wave; tile t-1 is free
+          const TileDma dma =
+              prep_tile(kv_begin + (t + kStages - 1) * kTileKeys, (t + kStages - 1) % kStages);
+          const char* stage = smem + (t % kStages) * kTileBytes;
+          float x[2][8];
+          scores(stage, q, x);
+          softmax<false>(x, kv_begin + t * kTileKeys, m_ref, m_seen, l_run, p);
+          pv(stage, p, o, &dma);
+        }
+        // The last (up to kStages-1) tiles: everything is issued; the very
+        // last one may be partial.
+        for (; t < ntiles; ++t) {
+          wait_tile(0);
           lds_barrier();
-          if (t + kStages - 1 < ntiles)
-            issue_tile(kv_begin + (t + kStages - 1) * kTileKeys, (t + kStages - 1) % kStages);
-          compute_tile(smem + (t % kStages) * kTileBytes, kv_begin + t * kTileKeys, q, o, m_ref,
-                       m_seen, l_run);
+          const char* stage = smem + (t % kStages) * kTileBytes;
+          float x[2][8];
+          scores(stage, q, x);
+          softmax<true>(x, kv_begin + t * kTileKeys, m_ref, m_seen, l_run, p);
+          pv(stage, p, o);
         }
         // Redo the item if any head of the workgroup overflowed its reference.
         int* flags = reinterpret_cast<int*>(smem + kStages * kTileBytes);
@@ -260,65 +365,120 @@ struct Attn {
     }
   }
 
-  __device__ __forceinline__ void compute_tile(const char* K, int base,
-                                               const bf16x8_t (&q)[kQChunks],
-                                               f32x16_t (&o)[kLoraRank / 32], float& m_ref,
-                                               float& m_seen, float& l_run) const {
-    // S^T[key, head] over the 576 latent dims.
-    f32x16_t s;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) s[j] = 0.f;
-    // Operands are read kAhead k-steps before their MFMA, so LDS latency
-    // overlaps the MFMA pipeline.
+  // S^T of the tile in stage K: four 16x16x32 accumulator chains
+  // acc[kb][hb] (keys 16kb.., heads 16hb..), operands read kAhead k-steps
+  // early; then the lane^16 exchange.  On return x[ks][e] is the score of
+  // key 16ks + 8(lane/32) + e for head lane%32.
+  __device__ __forceinline__ void scores(const char* K, const bf16x8_t (&q)[2][kQSteps],
+                                         float (&x)[2][8]) const {
+    constexpr int kAhead = 2;
     const char* kq = K + qk_off;
-    constexpr int kAhead = 3;
-    bf16x8_t kbuf[kAhead];
+    auto kload = [&](int ks, int kb) {
+      return *reinterpret_cast<const bf16x8_t*>(kq + ks * 2048 + kb * 256);
+    };
+    f32x4_t acc[2][2];
 #pragma unroll
-    for (int i = 0; i < kAhead; ++i) kbuf[i] = *reinterpret_cast<const bf16x8_t*>(kq + i * 1024);
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int kk = 0; kk < kQChunks; ++kk) {
-      const bf16x8_t kv = kbuf[kk % kAhead];
-      if (kk + kAhead < kQChunks)
-        kbuf[kk % kAhead] = *reinterpret_cast<const bf16x8_t*>(kq + (kk + kAhead) * 1024);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, q[kk], s, 0, 0, 0);
+      for (int hb = 0; hb < 2; ++hb) acc[kb][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    bf16x8_t kbuf[kAhead][2];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) {
+      kbuf[i][0] = kload(i, 0);
+      kbuf[i][1] = kload(i, 1);
     }
-    // Keep the reads kAhead steps ahead: the scheduler would otherwise pull
-    // each read down next to its MFMA.
-    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);  // DS reads
 #pragma unroll
-    for (int kk = 0; kk < kQChunks; ++kk) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      if (kk + kAhead < kQChunks) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one DS read
+    for (int ks = 0; ks < kQSteps; ++ks) {
+      const bf16x8_t k0 = kbuf[ks % kAhead][0], k1 = kbuf[ks % kAhead][1];
+      if (ks + kAhead < kQSteps) {
+        kbuf[ks % kAhead][0] = kload(ks + kAhead, 0);
+        kbuf[ks % kAhead][1] = kload(ks + kAhead, 1);
+      }
+      acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, q[0][ks], acc[0][0], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, q[0][ks], acc[1][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, q[1][ks], acc[0][1], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, q[1][ks], acc[1][1], 0, 0, 0);
     }
-    // Scale to base 2, mask keys beyond the item's range, tile max.
-    float x[16];
+    // Keep the reads kAhead k-steps ahead of their MFMAs.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);  // DS reads
+#pragma unroll
+    for (int ks = 0; ks < kQSteps; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // four MFMAs
+      if (ks + kAhead < kQSteps) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    // acc[kb][hb][i] is key 16kb + 4(lane/16) + i of head 16hb + lane%16.
+    // Lane l keeps head block hb_t = (l/16)%2 (its head l%32) and trades the
+    // other block with lane l^16, whose head it is.
+    const int g4 = lane >> 4;
+    const bool odd = g4 & 1;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float own = odd ? acc[kb][1][i] : acc[kb][0][i];
+        const float give = odd ? acc[kb][0][i] : acc[kb][1][i];
+        const float got = __shfl_xor(give, 16);
+        x[kb][i] = odd ? got : own;      // keys 16kb + 8(l/32) + i
+        x[kb][4 + i] = odd ? own : got;  // keys 16kb + 8(l/32) + 4 + i
+      }
+    }
+  }
+
+  // Softmax of one tile's scores against the item's reference maximum:
+  // p = 2^(s * scale_log2 - m_ref) as the bf16 P^T operand (x[ks][e] is key
+  // 16ks + 8 half + e of the lane's head).
+  template <bool kMask>
+  __device__ __forceinline__ void softmax(float (&x)[2][8], int base, float& m_ref,
+                                          float& m_seen, float& l_run, bf16x8_t (&p)[2]) const {
     float mx = -INFINITY;
+    if (!kMask || base + kTileKeys <= kv_end) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int key = base + 8 * (j >> 2) + 4 * half + (j & 3);
-      x[j] = key < kv_end ? s[j] * a.scale_log2 : -INFINITY;
-      mx = fmaxf(mx, x[j]);
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, x[ks][e]);
+    } else {  // the item's last tile: mask keys beyond its range
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = base + 16 * ks + 8 * half + e;
+          x[ks][e] = key < kv_end ? x[ks][e] : -INFINITY;
+          mx = fmaxf(mx, x[ks][e]);
+        }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
     m_seen = fmaxf(m_seen, mx);
     if (m_ref == -INFINITY) m_ref = mx;  // first tile of the item: O is still zero
-    // Probabilities relative to the reference, as the bf16 B operand.
-    bf16x8_t p[2];
+    const float neg_ref = -m_ref;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float e = __builtin_amdgcn_exp2f(fminf(x[j] - m_ref, kMaxExponent));
-      l_run += e;
-      p[j >> 3][j & 7] = static_cast<__bf16>(e);
-    }
-    // O^T[col, head] += V^T[col, key] . P^T[key, head].
-    const char* kv = K + pv_off;
-    auto vload = [&](int step) {
-      const char* ptr = kv + (step >> 1) * 2048 + (step & 1) * 256;
-      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(ptr));
-      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(ptr + 128));
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = __builtin_amdgcn_exp2f(
+            fminf(__builtin_fmaf(x[ks][e], a.scale_log2, neg_ref), kMaxExponent));
+        l_run += v;
+        p[ks][e] = static_cast<__bf16>(v);
+      }
+  }
+
+  // O^T += V^T . P^T for the tile in stage K: 32 MFMAs over 16 independent
+  // accumulators (key half outermost, so consecutive MFMAs never depend on
+  // each other); operands read kAhead steps early.  With `dma`, the next
+  // tile's DMAs go out one every third MFMA, so their issue overlaps the
+  // MFMA pipe instead of stalling the wave in one burst.
+  __device__ __forceinline__ void pv(const char* K, const bf16x8_t (&p)[2],
+                                     f32x16_t (&o)[kLoraRank / 32],
+                                     const TileDma* dma = nullptr) const {
+    constexpr int kAhead = 3;
+    constexpr int kSteps = 2 * (kLoraRank / 32);
+    const char* kv0 = K + pv_off0;
+    const char* kv1 = K + pv_off1;
+    auto vload = [&](int st) {  // column block st % 16, key half st / 16
+      const int off = (st & 15) * 2048 + (st >> 4) * 256;
+      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(kv0 + off));
+      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(kv1 + off));
       return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    constexpr int kSteps = 2 * (kLoraRank / 32);  // (column block, key half) pairs
     bf16x8_t vbuf[kAhead];
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) vbuf[i] = vload(i);
@@ -326,7 +486,12 @@ struct Attn {
     for (int st = 0; st < kSteps; ++st) {
       const bf16x8_t v = vbuf[st % kAhead];
       if (st + kAhead < kSteps) vbuf[st % kAhead] = vload(st + kAhead);
-      o[st >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, p[st & 1], o[st >> 1], 0, 0, 0);
+      o[st & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, p[st >> 4], o[st & 15], 0, 0, 0);
+      if (dma && (st % 3) == 2 && st / 3 < kLoadsPerWave) issue_one(*dma, st / 3);
+    }
+    if (dma) {  // waves of fewer than 4 per workgroup issue more DMAs per tile
+#pragma unroll
+      for (int j = kSteps / 3; j < kLoadsPerWave; ++j) issue_one(*dma, j);
     }
   }
 
@@ -401,28 +566,37 @@ struct Attn {
   }
 };
 
-template <int NW>
+template <int NW, bool kTileInPage>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attention_kernel(AttnArgs args) {
-  __shared__ __attribute__((aligned(1024))) char smem[kStages * kTileBytes + kFlagBytes];
-  Attn<NW> k(args, smem);
+  __shared__ __attribute__((aligned(1024)))
+  char smem[kStages * kTileBytes + kFlagBytes + kMaxItemPages * 4];
+  Attn<NW, kTileInPage> k(args, smem);
   k.run();
+}
+
+template <int NW>
+hipError_t launch_nw(const AttnArgs& a, int num_workers, hipStream_t stream) {
+  if (a.page_size % kTileKeys == 0)
+    hipLaunchKernelGGL((attention_kernel<NW, true>), dim3(num_workers), dim3(NW * kWave), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((attention_kernel<NW, false>), dim3(num_workers), dim3(NW * kWave), 0,
+                       stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a, int num_workers, hipStream_t stream) {
   if (num_workers <= 0) return hipSuccess;
-  const int nw = (a.num_heads + 31) / 32;
-  const dim3 grid(num_workers);
-  switch (nw) {
-    case 1: hipLaunchKernelGGL(attention_kernel<1>, grid, dim3(1 * kWave), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(attention_kernel<2>, grid, dim3(2 * kWave), 0, stream, a); break;
-    case 3: hipLaunchKernelGGL(attention_kernel<3>, grid, dim3(3 * kWave), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(attention_kernel<4>, grid, dim3(4 * kWave), 0, stream, a); break;
+  switch ((a.num_heads + 31) / 32) {
+    case 1: return launch_nw<1>(a, num_workers, stream);
+    case 2: return launch_nw<2>(a, num_workers, stream);
+    case 3: return launch_nw<3>(a, num_workers, stream);
+    case 4: return launch_nw<4>(a, num_workers, stream);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace mla

@@ -40,6 +40,9 @@ struct CostModel {
 };
 
 constexpr int kMinPieceTiles = 2;
+// Longest work item: the kernel stages an item's page ids (one per tile when
+// a tile never crosses a page) in a fixed LDS array of this many entries.
+constexpr int kMaxItemTiles = 1024;
 
 // Greedy contiguous fill of `budget` cost per worker.  Returns the number of
 // workers used (may exceed num_workers only if forced onto the last one,
@@ -61,26 +64,32 @@ void fill(const std::vector<TokenWork>& toks, const CostModel& cm, double budget
     bool split = false;
     while (a < tw.tiles) {
       const int rem = tw.tiles - a;
-      const double whole_cost = rem + cm.item + (split ? cm.split : 0.0);
       const double free = budget - load[k];
-      if (whole_cost <= free + kMinPieceTiles || k == num_workers - 1) {
+      const bool last = k == num_workers - 1;
+      // The whole remainder as one item, if it is not too long and fits.
+      if (rem <= kMaxItemTiles &&
+          (rem + cm.item + (split ? cm.split : 0.0) <= free + kMinPieceTiles || last)) {
         const int32_t kb = a * kTileKeys;
         (*per_worker)[k].push_back(WorkItem{tw.token, tw.row, kb, tw.visible, split ? 0 : -1, {0, 0, 0}});
-        load[k] += whole_cost;
+        load[k] += rem + cm.item + (split ? cm.split : 0.0);
         a = tw.tiles;
         break;
       }
-      const double space = free - cm.item - cm.split;
-      if (space >= kMinPieceTiles && rem - static_cast<int>(space) >= kMinPieceTiles) {
-        const int take = static_cast<int>(space);
+      // Otherwise a piece: at most kMaxItemTiles, and when it is cut for the
+      // budget, leave at least kMinPieceTiles for the rest.
+      int cap = rem > kMaxItemTiles ? kMaxItemTiles : rem - kMinPieceTiles;
+      int take = last ? cap : std::min(cap, static_cast<int>(free - cm.item - cm.split));
+      if (take >= kMinPieceTiles) {
         const int32_t kb = a * kTileKeys;
         (*per_worker)[k].push_back(
             WorkItem{tw.token, tw.row, kb, (a + take) * kTileKeys, 0, {0, 0, 0}});
         load[k] += take + cm.item + cm.split;
         a += take;
         split = true;
+        if (!last && load[k] >= budget - kMinPieceTiles) ++k;  // this worker is full
+        continue;
       }
-      ++k;  // this worker is full
+      ++k;  // no room left on this worker (never the last one here)
     }
     if (load[k] >= budget && k < num_workers - 1) ++k;
   }
