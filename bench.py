@@ -151,6 +151,20 @@ def cpu_baseline(w, target_s=10.0):
             "sample": f"whole decode batch (64 rows, H=128) x {reps} repeats, {el:.1f} s, fp64 numpy"}
 
 
+def copy_calibration(nbytes=1 << 30, reps=5):
+    """A plain device-to-device copy of known size, profiled beside the
+    attention kernel to scale the HBM traffic counters (FETCH_SIZE and
+    WRITE_SIZE) to bytes."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": nbytes, "bytes_written": nbytes,
+                      "reps": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -158,6 +172,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -168,6 +184,10 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     w = W.decode_batch()
     nbytes, flops = algorithmic(w)

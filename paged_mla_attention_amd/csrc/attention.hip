@@ -11,36 +11,41 @@
 //   * one workgroup per worker (one per compute unit); it runs the worker's
 //     items in order.  An item is one query token with ALL its heads, so a
 //     key tile staged in LDS is shared by every head of the token;
-//   * wave w owns heads [32w, 32w + 32); a workgroup has ceil(H / 32) waves;
+//   * NW = 1, 2 or 4 waves hold 32 NW head slots.  For the scores wave w owns
+//     heads [32w, 32w + 32) (its query rows stay in registers); for P . V it
+//     owns latent columns [512w/NW, 512(w+1)/NW) of EVERY head, taking the
+//     other waves' probabilities from LDS.  Splitting P . V by columns cuts
+//     each wave's transposed V reads by NW (a wave issues one transposing
+//     LDS read per ~24 cycles, which bounded a split by heads);
 //   * keys are processed in tiles of 32.  A tile is copied from HBM straight
-//     into LDS by global_load_lds (no staging registers), four tiles deep
-//     (4 x 36 KiB of the 160 KiB LDS), with explicit vmcnt waits and a bare
-//     s_barrier per tile;
+//     into LDS by global_load_lds (no staging registers) into four 36 KiB
+//     stages, with explicit vmcnt waits and one bare s_barrier per tile;
 //   * one swizzled LDS layout serves both products: 16-byte chunk (key, dc)
 //     (dc = 8-column chunk of the 576 latent columns) sits at
 //     (dc/2)*1024 + (dc%2)*512 + (key ^ 4*(dc%2) ^ 8*((dc/2)%2))*16, which
 //     the loader writes as 36 DMA instructions of 1 KiB and which keeps both
-//     read patterns free of bank conflicts on the 64-bank LDS (16 lanes per
-//     pass for 16-byte reads, 32 lanes for 8-byte reads);
+//     read patterns free of bank conflicts;
 //   * S^T = K . Q^T on v_mfma_f32_16x16x32_bf16: four independent
-//     accumulator chains (2 key blocks x 2 head blocks of 16), so the 18
-//     k-steps never wait on a previous MFMA's result.  One exchange of half
-//     the scores with lane^16 then leaves each lane with 16 scores of ONE
-//     head (lane l: head l%32, keys 16ks + 8(l/32) + e), so the softmax
-//     statistics are per lane plus one cross-lane max per tile;
+//     accumulator chains (2 key blocks x 2 head blocks of 16).  One exchange
+//     of half the scores with lane^16 leaves each lane with 16 scores of ONE
+//     head (lane l: head l%32, keys 16ks + 8(l/32) + e), already laid out as
+//     the P^T operand of the 32x32x16 MFMA;
 //   * O^T += V^T . P^T on v_mfma_f32_32x32x16_bf16 with latent columns as M
-//     and heads as N: the probabilities are the B operand as they stand, and
-//     the V^T operand is read from the same K tile with ds_read_b64_tr_b16,
-//     whose 16-lane transpose turns four 8-byte row pieces into one column
-//     each.  The 16 column blocks are independent accumulators;
+//     and heads as N; V^T is read from the same K tile with
+//     ds_read_b64_tr_b16, whose 16-lane transpose turns four 8-byte row
+//     pieces into one column each;
+//   * software pipeline: iteration t computes S(t), then the softmax of tile
+//     t (VALU) next to P . V of tile t-1 (MFMA), and publishes P(t) in one
+//     of two LDS buffers.  Tile t+2 is DMA'd during S(t);
 //   * softmax in base 2 against a per-head reference maximum fixed at the
 //     item's first tile: p = 2^(x - m_ref) is exact for any reference (output
 //     and LSE are normalised with the same value), so the O accumulators are
 //     never rescaled inside the key loop.  A later score more than 2^64 above
 //     the reference (which would overflow) makes the workgroup redo the item
 //     with the largest score seen as the reference;
-//   * page ids come through scalar loads, so no vector load inside the key
-//     loop ever forces the in-order vmcnt to drain the DMA queue;
+//   * page ids come through scalar loads issued one tile ahead, and the
+//     query rows through asm loads with one explicit wait, so nothing inside
+//     the key loop makes the in-order vmcnt drain the DMA queue;
 //   * items covering a token's whole key range write bf16 output + LSE;
 //     pieces of a split token write fp32 partials that a merge kernel combines.
 #include "kernels.h"
@@ -51,12 +56,9 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
-typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef short s16x4_t __attribute__((vector_size(8)));
-typedef short s16x8_t __attribute__((vector_size(16)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(4))) const int32_t const_i32_t;
 
 constexpr int kWave = 64;
@@ -64,46 +66,76 @@ constexpr int kQSteps = kLatentDim / 32;          // 18 k-steps of 32 over 576
 constexpr int kDmaPerTile = kLatentDim / 16;      // 36 x 1 KiB (two 16-B chunks x 32 keys)
 constexpr int kTileBytes = kDmaPerTile * 1024;    // 36864
 constexpr int kStages = 4;
-constexpr int kFlagBytes = 16;                    // per-wave redo flags after the stages
-constexpr int kMaxItemPages = 1024;               // page ids staged per item (tile-aligned pages)
-constexpr int kFinishRow = 128 + 4;               // floats per head row of the output staging
-constexpr int kFinishWaveBytes = (32 * kFinishRow + 32) * 4;  // per-wave staging + 1/l per head
+constexpr int kStageBytes = kStages * kTileBytes;
+constexpr int kPGroupBytes = 2 * kWave * 16;      // one wave's P^T operands of a tile
 constexpr float kMaxExponent = 64.0f;             // log2 headroom above the reference
 constexpr float kLn2 = 0.693147180559945309f;
 
-// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector
-// memory operations are outstanding and leaves the other counters alone.
+// s_waitcnt immediates (gfx9 encoding) that wait on one counter and leave
+// the others alone.
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+constexpr int kLgkmZero = 0xF | (0x7 << 4) | (0x3 << 14);
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
 // Barrier without the memory fence of __syncthreads (which would wait for
-// every outstanding LDS DMA); the empty asm keeps the compiler from moving
-// LDS accesses across it.
+// every outstanding LDS DMA): this wave's LDS accesses have completed, then
+// s_barrier.  The empty asm keeps the compiler from moving memory accesses
+// across it.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kLgkmZero);
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
+// Pins an MFMA operand to VGPRs: left alone, the register allocator may
+// load operands into AGPRs (MFMA accepts both), where they evict the
+// output accumulators.  Applied where the operand is used (the asm waits for
+// a pending load of it).
+__device__ __forceinline__ void in_vgpr(bf16x8_t& v) { asm("" : "+v"(v)); }
+
+// A per-call copy of a lane value the compiler cannot see through: address
+// arithmetic derived from it stays where it is used instead of being hoisted
+// out of the item loop, where it would occupy (and spill) registers for the
+// whole kernel.
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 template <int NW, bool kTileInPage>
 struct Attn {
-  static constexpr int kLoadsPerWave = (kDmaPerTile + NW - 1) / NW;
-  static constexpr int kWaitOne = kLoadsPerWave > 63 ? 63 : kLoadsPerWave;
+  static constexpr int kDimBlocks = (kLoraRank / 32) / NW;  // 32-column blocks of O per wave
+  static constexpr int kLoadsPerWave = kDmaPerTile / NW;    // DMA instructions per tile per wave
+  static_assert(kDmaPerTile % NW == 0 && (kLoraRank / 32) % NW == 0, "NW must be 1, 2 or 4");
+  static_assert(kLoadsPerWave <= 63, "vmcnt holds at most 63");
   static constexpr int kWaitTwo = 2 * kLoadsPerWave > 63 ? 63 : 2 * kLoadsPerWave;
+  static constexpr int kPBufBytes = NW * kPGroupBytes;
+  static constexpr int kFlagOff = kStageBytes + kPBufBytes;  // per-wave redo flags
+  // Page ids of the current item (tiles that never span pages): an item has
+  // at most kMaxItemTiles tiles, so at most that many pages.
+  static constexpr int kPageOff = kFlagOff + 16;
+  static constexpr int kPageLoads = (kMaxItemTiles + NW * kWave - 1) / (NW * kWave);
+  static constexpr int kLdsBytes = kPageOff + (kTileInPage ? kMaxItemTiles * 4 : 16);
+  // Output staging in the idle stages: per wave, 32 head rows of its columns.
+  static constexpr int kFinRow = kDimBlocks * 32 + 4;  // floats (padding staggers banks)
+  static constexpr int kFinWaveBytes = 32 * kFinRow * 4;
+  static constexpr int kXchgOff = NW * kFinWaveBytes;  // 1/l of every head slot
+  static_assert(kXchgOff + 32 * NW * 4 <= kStageBytes, "finish staging fits the stages");
 
   const AttnArgs& a;
   char* smem;
   int lane, l32, half, wave, head;
   bool head_ok;
   int ld_key, ld_off, qk_off, pv_off0, pv_off1;  // per-lane LDS / row offsets
-  uint32_t lds_base;                   // LDS address of the stages
+  uint32_t lds_base;                               // LDS address of the stages
   // current item
-  int token, kv_end, slot;
+  int token, kv_begin, kv_end, slot;
   int page_base;   // index of the row's first page in kv_indices
-  int first_page;  // row page index of the item's first key (tile-aligned pages)
+  int first_page;  // row page index of the item's first key
 
   __device__ Attn(const AttnArgs& args, char* s) : a(args), smem(s) {
     const int tid = threadIdx.x;
@@ -137,17 +169,27 @@ struct Attn {
     pv_off1 = pv_base + ((8 * (g2 ^ cg) + 4 * (1 ^ par) + (sl >> 2)) * 16);
   }
 
-  // Page id of key `key` of the current row, for the lane's own key.  The
-  // page table is read with scalar loads only (wave-uniform addresses, made
-  // explicit with readfirstlane so no select is folded into a per-lane
-  // address): a vector load here would make the in-order vmcnt wait for every
-  // DMA in flight.
+  __device__ __forceinline__ char* pbuf() const { return smem + kStageBytes; }
+  __device__ __forceinline__ const char* stage(int t) const {
+    return smem + (t % kStages) * kTileBytes;
+  }
+
+  // Page id of tile t of the item, from the item's page list in LDS (as a
+  // VGPR value; the caller makes it uniform where it uses it).  LDS reads
+  // keep the compiler's lgkmcnt waits exact, where a scalar load in flight
+  // would make every LDS wait a full drain.
+  __device__ __forceinline__ int tile_page_v(int t) const {
+    const int* pl = reinterpret_cast<const int*>(smem + kPageOff);
+    return pl[(kv_begin + t * kTileKeys) / a.page_size - first_page];
+  }
+
+  // Page id for the lane's own key `key` of the tile starting at `base`
+  // when a tile can span pages: 32 scalar loads and a select (a vector load
+  // here would make the in-order vmcnt wait for every DMA in flight).
   __device__ __forceinline__ int lane_page(int base, int key) const {
     const int P = a.page_size;
     const_i32_t* idx = (const_i32_t*)(a.kv_indices) + page_base;
     const int first = base / P;
-    if (kTileInPage)  // page_size % 32 == 0: the whole tile is in one page
-      return __builtin_amdgcn_readfirstlane(idx[first]);
     const int j = key / P - first;  // 0 .. 31
     int v = __builtin_amdgcn_readfirstlane(idx[first]);
 #pragma unroll
@@ -158,99 +200,111 @@ struct Attn {
     return v;
   }
 
-  // One 16-byte-per-lane DMA from global memory into LDS at lds_addr + 16 *
-  // lane.  Issued through asm so that the compiler, which cannot tell the
-  // stages apart, does not make later LDS reads wait for every DMA; the
-  // tile pipeline waits on vmcnt itself.  M0 holds the LDS base; one wait
-  // state separates its write from the DMA.  Volatile asm keeps its order
-  // against the barriers (also volatile asm); the stage it writes is not
-  // read before the next barrier.
+  // One 16-byte-per-lane DMA from global memory into LDS at
+  // m0 + offset + 16 * lane:
+  // lane row address (64-bit VGPR pair, `off` form) or a uniform base (SGPR
+  // pair) plus a 32-bit lane offset, each with a constant byte offset.
+  // Issued through asm so that the compiler, which cannot tell the stages
+  // apart, does not make later LDS reads wait for every DMA; the tile
+  // pipeline waits on vmcnt itself.  One wait state separates the M0 write
+  // from the DMA.  The stage it writes is not read before the next barrier.
+  // The uniform operands pass through readfirstlane so that they are SGPRs
+  // even where the compiler cannot prove them uniform.
+  template <int kOff>
   __device__ __forceinline__ static void dma16(const char* src, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2"
                  :
-                 : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+                 : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "i"(kOff)
                  : "m0");
   }
-
-  // The same DMA with a uniform 64-bit base (SGPR pair) and a 32-bit lane
-  // offset, for tiles that lie in one page.
-  // Both uniform operands pass through readfirstlane so that they are SGPRs
-  // even where the compiler cannot prove them uniform.
+  template <int kOff>
   __device__ __forceinline__ static void dma16s(uint32_t voff, const char* sbase,
                                                 uint32_t lds_addr) {
     const uint64_t b = reinterpret_cast<uint64_t>(sbase);
     const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
     const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32));
     const uint64_t sb = (static_cast<uint64_t>(hi) << 32) | lo;
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3"
                  :
-                 : "v"(voff), "s"(sb), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+                 : "v"(voff), "s"(sb), "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "i"(kOff)
                  : "m0");
   }
 
-  // Source rows and LDS destination of one tile's DMAs for this lane: even
-  // DMA instructions fetch key ld_key, odd ones key ld_key ^ 8.  Keys beyond
-  // the item's range re-read its last key (finite data, masked later).
+  // One tile's DMAs for this wave.  DMA instruction I = wave + j NW covers
+  // 16-byte chunks 2I and 2I+1 (lane halves) of the 32 keys: lane p fetches
+  // key (p%32) ^ 4(p/32) ^ 8(I%2) into LDS at 1024 I + 16 p.  The wave's
+  // share of the row offset (32 I bytes) splits into a per-wave part folded
+  // into the lane address and a constant per instruction.  Keys beyond the
+  // item's range re-read its last key (finite data, masked later).
   struct TileDma {
-    const char* src_e;  // general pages: per-lane row addresses
-    const char* src_o;
+    const char* src_e;  // tiles that may span pages: lane row address for
+    const char* src_o;  //   even / odd I (+ 32 wave)
     const char* sbase;  // tile in one page: page base (uniform) ...
-    uint32_t voff_e;    // ... and the row offsets of the even / odd DMAs' key
+    uint32_t voff_e;    // ... and the lane row offsets for even / odd I
     uint32_t voff_o;
-    uint32_t dst;
+    uint32_t dst;       // LDS address of DMA I = wave
   };
 
-  __device__ __forceinline__ TileDma prep_tile(int base, int stage) const {
+  // Tile t of the item; `pg` is the page of its first key (used when tiles
+  // never span pages).
+  __device__ __forceinline__ TileDma prep_tile(int t, int pg) const {
     const int P = a.page_size;
+    const int base = kv_begin + t * kTileKeys;
     int ke = base + ld_key, ko = base + (ld_key ^ 8);
     ke = ke < kv_end ? ke : kv_end - 1;
     ko = ko < kv_end ? ko : kv_end - 1;
     TileDma d;
-    d.dst = lds_base + stage * kTileBytes;
-    if (kTileInPage) {  // one page id per tile, staged in LDS for the item
-      const int pg = __builtin_amdgcn_readfirstlane(page_lds()[base / P - first_page]);
+    d.dst = lds_base + (t % kStages) * kTileBytes + wave * 1024;
+    if (kTileInPage) {  // the tile lies in page pg: key k is row k - base + base % P
+      const int in_page = base % P;
       d.sbase = reinterpret_cast<const char*>(a.kv_cache + static_cast<int64_t>(pg) * P * kLatentDim);
-      d.voff_e = static_cast<uint32_t>((ke % P) * (kLatentDim * 2) + ld_off);
-      d.voff_o = static_cast<uint32_t>((ko % P) * (kLatentDim * 2) + ld_off);
+      d.voff_e = static_cast<uint32_t>((in_page + ke - base) * (kLatentDim * 2) + ld_off + wave * 32);
+      d.voff_o = static_cast<uint32_t>((in_page + ko - base) * (kLatentDim * 2) + ld_off + wave * 32);
       d.src_e = d.src_o = nullptr;
     } else {
       const int pe = lane_page(base, ke), po = lane_page(base, ko);
       d.src_e = reinterpret_cast<const char*>(
-          a.kv_cache + (static_cast<int64_t>(pe) * P + ke % P) * kLatentDim) + ld_off;
+          a.kv_cache + (static_cast<int64_t>(pe) * P + ke % P) * kLatentDim) + ld_off + wave * 32;
       d.src_o = reinterpret_cast<const char*>(
-          a.kv_cache + (static_cast<int64_t>(po) * P + ko % P) * kLatentDim) + ld_off;
+          a.kv_cache + (static_cast<int64_t>(po) * P + ko % P) * kLatentDim) + ld_off + wave * 32;
       d.sbase = nullptr;
       d.voff_e = d.voff_o = 0;
     }
     return d;
   }
 
-  // DMA instruction j (0 .. kLoadsPerWave-1) of this wave for a tile.
-  __device__ __forceinline__ void issue_one(const TileDma& d, int j) const {
-    const int I = wave + j * NW;
-    if (NW * kLoadsPerWave == kDmaPerTile || I < kDmaPerTile) {
-      if (kTileInPage)  // (with an even number of waves I has this wave's parity)
-        dma16s(((I & 1) ? d.voff_o : d.voff_e) + I * 32, d.sbase, d.dst + I * 1024);
-      else
-        dma16(((I & 1) ? d.src_o : d.src_e) + I * 32, d.dst + I * 1024);
+  // DMA instruction I = wave + j NW of this wave for a tile.  With an even
+  // number of waves I has the wave's parity; with one wave, j's.
+  template <int j>
+  __device__ __forceinline__ void issue_one(const TileDma& d) const {
+    constexpr int kOff = j * NW * 32;
+    // The instruction offset moves the LDS destination as well as the
+    // global address, so M0 takes it back off.
+    const uint32_t dst = d.dst + j * NW * 1024 - kOff;
+    const bool odd = NW == 1 ? (j & 1) : (wave & 1);
+    if (kTileInPage)
+      dma16s<kOff>(odd ? d.voff_o : d.voff_e, d.sbase, dst);
+    else
+      dma16<kOff>(odd ? d.src_o : d.src_e, dst);
+  }
+
+  template <int j0, int j1>
+  __device__ __forceinline__ void issue_range(const TileDma& d) const {
+    if constexpr (j0 < j1) {
+      issue_one<j0>(d);
+      issue_range<j0 + 1, j1>(d);
     }
   }
 
-  __device__ __forceinline__ void issue_tile(int base, int stage) const {
-    const TileDma d = prep_tile(base, stage);
-#pragma unroll
-    for (int j = 0; j < kLoadsPerWave; ++j) issue_one(d, j);
+  __device__ __forceinline__ void issue_tile(int t, int pg) const {
+    const TileDma d = prep_tile(t, pg);
+    issue_range<0, kLoadsPerWave>(d);
   }
 
-  __device__ __forceinline__ int* page_lds() const {
-    return reinterpret_cast<int*>(smem + kStages * kTileBytes + kFlagBytes);
-  }
-
-  // Wait until this wave's DMAs for the tile `later` tiles before the newest
-  // have landed.
-  __device__ __forceinline__ void wait_tile(int later) const {
+  // Waits for this wave's DMAs except those of the `later` newest tiles.
+  __device__ __forceinline__ static void wait_vm(int later) {
     if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kWaitTwo));
-    else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kWaitOne));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerWave));
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   }
 
@@ -264,113 +318,147 @@ struct Attn {
       const_i32_t* item = (const_i32_t*)(a.items) + it * 8;  // WorkItem fields
       token = item[0];
       const int row = item[1];
-      const int kv_begin = item[2];
+      kv_begin = item[2];
       kv_end = item[3];
       slot = item[4];
       page_base = ((const_i32_t*)(a.kv_indptr))[row];
-
-      // Query as the B operand of the 16x16x32 score MFMAs: for head block
-      // hb, lane (l16, g4) holds head 32 wave + 16 hb + l16, dims
-      // 32 ks + 8 g4 .. +8.  Padding heads read head 0's row and zero it.
-      bf16x8_t q[2][kQSteps];
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const int h = wave * 32 + hb * 16 + (lane & 15);
-        const bool ok = h < H;
-        const int hq = ok ? h : 0;
-        const uint16_t* qn = a.q_nope + (static_cast<int64_t>(token) * H + hq) * kLoraRank;
-        const uint16_t* qp = a.q_pe + (static_cast<int64_t>(token) * H + hq) * kRopeDim;
-        const unsigned keep = ok ? 0xFFFFFFFFu : 0u;
-        const int dl = 8 * (lane >> 4);
-#pragma unroll
-        for (int ks = 0; ks < kQSteps; ++ks) {
-          u32x4_t v = ks < kLoraRank / 32
-                          ? *reinterpret_cast<const u32x4_t*>(qn + ks * 32 + dl)
-                          : *reinterpret_cast<const u32x4_t*>(qp + (ks - kLoraRank / 32) * 32 + dl);
-          v &= keep;
-          q[hb][ks] = __builtin_bit_cast(bf16x8_t, v);
-        }
-      }
-
-      f32x16_t o[kLoraRank / 32];
-      float m_ref = -INFINITY;  // reference max of scaled base-2 scores (per head)
-      float m_seen = -INFINITY; // largest score seen (per head)
-      float l_run = 0.f;        // this lane's share of the softmax denominator
       const int ntiles = (kv_end - kv_begin + kTileKeys - 1) / kTileKeys;
+
+      f32x16_t o[NW][kDimBlocks];
+      float m_ref = -INFINITY;  // reference max of scaled base-2 scores (per head)
+      float m_seen = -INFINITY; // largest scaled score seen by this lane
+      float l_run = 0.f;        // this lane's share of the softmax denominator
       for (;;) {
 #pragma unroll
-        for (int mb = 0; mb < kLoraRank / 32; ++mb)
+        for (int g = 0; g < NW; ++g)
 #pragma unroll
-          for (int j = 0; j < 16; ++j) o[mb][j] = 0.f;
+          for (int db = 0; db < kDimBlocks; ++db)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) o[g][db][j] = 0.f;
         l_run = 0.f;
+        m_seen = -INFINITY;
         if (ntiles == 0) break;
-        // Every wave is done with the previous item's output staging and
-        // page ids (LDS); then this item's page ids are staged, and this
-        // wave's query loads and earlier stores retire before the DMA queue
-        // is counted tile by tile.
-        __syncthreads();
         if (kTileInPage) {
+          // Stage the item's page ids in LDS; the loads go out before the
+          // barrier that waits for the previous item's LDS users.
           const int P = a.page_size;
           first_page = kv_begin / P;
-          const int n = (kv_end - 1) / P - first_page + 1;  // <= kMaxItemPages
-          for (int i = threadIdx.x; i < n; i += NW * kWave)
-            page_lds()[i] = a.kv_indices[page_base + first_page + i];
-          __syncthreads();
+          const int n = (kv_end - 1) / P - first_page + 1;  // <= kMaxItemTiles
+          int pv[kPageLoads];
+#pragma unroll
+          for (int k = 0; k < kPageLoads; ++k) {
+            const int i = threadIdx.x + k * NW * kWave;
+            pv[k] = i < n ? reinterpret_cast<const int32_t*>(a.kv_indices)[page_base + first_page + i] : 0;
+          }
+          lds_barrier();
+          int* pl = reinterpret_cast<int*>(smem + kPageOff);
+#pragma unroll
+          for (int k = 0; k < kPageLoads; ++k) {
+            const int i = threadIdx.x + k * NW * kWave;
+            if (i < n) pl[i] = pv[k];
+          }
         }
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        asm volatile("" ::: "memory");
+        // Every wave is done with the previous item's (or attempt's) LDS,
+        // and the page list is complete.
+        lds_barrier();
 #pragma unroll
         for (int t = 0; t < kStages - 1; ++t)
-          if (t < ntiles) issue_tile(kv_begin + t * kTileKeys, t);
-        bf16x8_t p[2];
-        // Steady state (straight-line body): tile t has kStages-2 later
-        // tiles in flight; tile t+3 is issued into the stage tile t-1 used.
-        const int steady = ntiles - (kStages - 1);
-        int t = 0;
-        for (; t < steady; ++t) {
-          wait_tile(kStages - 2);  // tile t has landed ...
-          lds_barrier();           // ... for every wave; tile t-1 is free
-          const TileDma dma =
-              prep_tile(kv_begin + (t + kStages - 1) * kTileKeys, (t + kStages - 1) % kStages);
-          const char* stage = smem + (t % kStages) * kTileBytes;
-          float x[2][8];
-          scores(stage, q, x);
-          softmax<false>(x, kv_begin + t * kTileKeys, m_ref, m_seen, l_run, p);
-          pv(stage, p, o, &dma);
+          if (t < ntiles)
+            issue_tile(t, kTileInPage ? __builtin_amdgcn_readfirstlane(tile_page_v(t)) : 0);
+        int pg_next = kTileInPage && ntiles > kStages - 1 ? tile_page_v(kStages - 1) : 0;
+        // Query as the B operand of the 16x16x32 score MFMAs: for head block
+        // hb, lane (l16, g4) holds head 32 wave + 16 hb + l16, dims
+        // 32 ks + 8 g4 .. +8.  Padding heads (beyond H) compute with head 0's
+        // row; their results are never stored.  Loaded after the first
+        // tiles' DMAs (the memory clobber keeps that order), so the
+        // compiler's waits for these loads also cover the DMAs before them.
+        asm volatile("" ::: "memory");
+        // (A redo attempt loads them again.)
+        u32x4_t q[2][kQSteps];
+        {
+          const int qlane = opaque(lane);
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            const int h = wave * 32 + hb * 16 + (qlane & 15);
+            const int hq = h < H ? h : 0;
+            const uint16_t* qn = a.q_nope + (static_cast<int64_t>(token) * H + hq) * kLoraRank;
+            const uint16_t* qp = a.q_pe + (static_cast<int64_t>(token) * H + hq) * kRopeDim;
+            const int dl = 8 * (qlane >> 4);
+#pragma unroll
+            for (int ks = 0; ks < kQSteps; ++ks)
+              q[hb][ks] = ks < kLoraRank / 32
+                              ? *reinterpret_cast<const u32x4_t*>(qn + ks * 32 + dl)
+                              : *reinterpret_cast<const u32x4_t*>(qp + (ks - kLoraRank / 32) * 32 + dl);
+          }
         }
-        // The last (up to kStages-1) tiles: everything is issued; the very
-        // last one may be partial.
-        for (; t < ntiles; ++t) {
-          wait_tile(0);
+        // Tile t: S(t) (with the DMAs of tile t+3 in between), softmax,
+        // P(t) published in LDS, then this wave's columns of P . V for every
+        // head.  Barriers: tile t landed for every wave and P . V of t-1
+        // done (its stage and the P buffer are free); P(t) complete.  One
+        // loop body for every tile (uniform branches for the first tile, the
+        // DMAs and the partial last tile) keeps the code and its register
+        // allocation single.
+        for (int t = 0; t < ntiles; ++t) {
+          wait_vm(ntiles - 1 - t);
           lds_barrier();
-          const char* stage = smem + (t % kStages) * kTileBytes;
+          const bool dma = t + kStages - 1 < ntiles;
+          TileDma d;
+          if (dma) {
+            d = prep_tile(t + kStages - 1, kTileInPage ? __builtin_amdgcn_readfirstlane(pg_next) : 0);
+            if (kTileInPage) {  // the next tile's page id, read a tile ahead
+              const int tn = t + kStages < ntiles ? t + kStages : ntiles - 1;
+              pg_next = tile_page_v(tn);
+            }
+          }
           float x[2][8];
-          scores(stage, q, x);
-          softmax<true>(x, kv_begin + t * kTileKeys, m_ref, m_seen, l_run, p);
-          pv(stage, p, o);
+          scores(stage(t), q, x, dma, d);
+          bf16x8_t p[2];
+          softmax(x, kv_begin + t * kTileKeys, t == 0, m_ref, m_seen, l_run, p);
+          store_p(p);
+          lds_barrier();
+          pv(stage(t), o);
         }
         // Redo the item if any head of the workgroup overflowed its reference.
-        int* flags = reinterpret_cast<int*>(smem + kStages * kTileBytes);
+        int* flags = reinterpret_cast<int*>(smem + kFlagOff);
         const bool redo = __any(m_seen > m_ref + kMaxExponent);
         if (lane == 0) flags[wave] = redo ? 1 : 0;
-        __syncthreads();
+        lds_barrier();
         int any_redo = 0;
 #pragma unroll
         for (int w = 0; w < NW; ++w) any_redo |= flags[w];
-        __syncthreads();
         if (!any_redo) break;
-        m_ref = m_seen;
+        m_ref = fmaxf(m_seen, __shfl_xor(m_seen, 32));  // the head's largest score
       }
       finish(o, m_ref, l_run);
     }
   }
 
+  __device__ __forceinline__ void store_p(const bf16x8_t (&p)[2]) const {
+    char* pb = pbuf();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      *reinterpret_cast<bf16x8_t*>(pb + wave * kPGroupBytes + ks * (kWave * 16) + lane * 16) = p[ks];
+  }
+
+  // The DMAs of k-step ks (of 18) of a score pass, spread evenly.
+  template <int ks = 0>
+  __device__ __forceinline__ void dma_step_ct(const TileDma& d, int k) const {
+    if constexpr (ks < kQSteps) {
+      if (k == ks)
+        issue_range<ks * kLoadsPerWave / kQSteps, (ks + 1) * kLoadsPerWave / kQSteps>(d);
+      else
+        dma_step_ct<ks + 1>(d, k);
+    }
+  }
+  __device__ __forceinline__ void dma_step(const TileDma& d, int ks) const { dma_step_ct<0>(d, ks); }
+
   // S^T of the tile in stage K: four 16x16x32 accumulator chains
   // acc[kb][hb] (keys 16kb.., heads 16hb..), operands read kAhead k-steps
-  // early; then the lane^16 exchange.  On return x[ks][e] is the score of
-  // key 16ks + 8(lane/32) + e for head lane%32.
-  __device__ __forceinline__ void scores(const char* K, const bf16x8_t (&q)[2][kQSteps],
-                                         float (&x)[2][8]) const {
+  // early; with dma a later tile's DMAs go out between the k-steps.  Then
+  // the lane^16 exchange.  On return x[ks][e] is the score of key
+  // 16ks + 8(lane/32) + e for head lane%32.
+  __device__ __forceinline__ void scores(const char* K, const u32x4_t (&q)[2][kQSteps],
+                                         float (&x)[2][8], bool dma, const TileDma& d) const {
     constexpr int kAhead = 2;
     const char* kq = K + qk_off;
     auto kload = [&](int ks, int kb) {
@@ -389,22 +477,21 @@ struct Attn {
     }
 #pragma unroll
     for (int ks = 0; ks < kQSteps; ++ks) {
-      const bf16x8_t k0 = kbuf[ks % kAhead][0], k1 = kbuf[ks % kAhead][1];
+      bf16x8_t k0 = kbuf[ks % kAhead][0], k1 = kbuf[ks % kAhead][1];
+      in_vgpr(k0);  // (at the use: the asm waits for the load)
+      in_vgpr(k1);
       if (ks + kAhead < kQSteps) {
         kbuf[ks % kAhead][0] = kload(ks + kAhead, 0);
         kbuf[ks % kAhead][1] = kload(ks + kAhead, 1);
       }
-      acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, q[0][ks], acc[0][0], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, q[0][ks], acc[1][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, q[1][ks], acc[0][1], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, q[1][ks], acc[1][1], 0, 0, 0);
-    }
-    // Keep the reads kAhead k-steps ahead of their MFMAs.
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);  // DS reads
-#pragma unroll
-    for (int ks = 0; ks < kQSteps; ++ks) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // four MFMAs
-      if (ks + kAhead < kQSteps) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, __builtin_bit_cast(bf16x8_t, q[0][ks]), acc[0][0], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, __builtin_bit_cast(bf16x8_t, q[0][ks]), acc[1][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, __builtin_bit_cast(bf16x8_t, q[1][ks]), acc[0][1], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, __builtin_bit_cast(bf16x8_t, q[1][ks]), acc[1][1], 0, 0, 0);
+      if (dma) dma_step(d, ks);  // this k-step's share of the DMAs
+      // Keep each k-step's reads kAhead steps ahead instead of letting the
+      // scheduler hoist all 36 (they would not fit in registers).
+      __builtin_amdgcn_sched_barrier(0);
     }
     // acc[kb][hb][i] is key 16kb + 4(lane/16) + i of head 16hb + lane%16.
     // Lane l keeps head block hb_t = (l/16)%2 (its head l%32) and trades the
@@ -426,29 +513,31 @@ struct Attn {
 
   // Softmax of one tile's scores against the item's reference maximum:
   // p = 2^(s * scale_log2 - m_ref) as the bf16 P^T operand (x[ks][e] is key
-  // 16ks + 8 half + e of the lane's head).
-  template <bool kMask>
-  __device__ __forceinline__ void softmax(float (&x)[2][8], int base, float& m_ref,
+  // 16ks + 8 half + e of the lane's head).  The first tile of an attempt
+  // fixes the reference (unless a redo has set it); keys past the item's end
+  // (last tile only) get probability 0.
+  __device__ __forceinline__ void softmax(float (&x)[2][8], int base, bool first, float& m_ref,
                                           float& m_seen, float& l_run, bf16x8_t (&p)[2]) const {
-    float mx = -INFINITY;
-    if (!kMask || base + kTileKeys <= kv_end) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, x[ks][e]);
-    } else {  // the item's last tile: mask keys beyond its range
+    if (base + kTileKeys > kv_end) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int key = base + 16 * ks + 8 * half + e;
           x[ks][e] = key < kv_end ? x[ks][e] : -INFINITY;
-          mx = fmaxf(mx, x[ks][e]);
         }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, x[ks][e]);
+    mx *= a.scale_log2;
     m_seen = fmaxf(m_seen, mx);
-    if (m_ref == -INFINITY) m_ref = mx;  // first tile of the item: O is still zero
+    if (first) {
+      const float mh = fmaxf(mx, __shfl_xor(mx, 32));
+      if (m_ref == -INFINITY) m_ref = mh;  // O is still zero
+    }
     const float neg_ref = -m_ref;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -461,106 +550,133 @@ struct Attn {
       }
   }
 
-  // O^T += V^T . P^T for the tile in stage K: 32 MFMAs over 16 independent
-  // accumulators (key half outermost, so consecutive MFMAs never depend on
-  // each other); operands read kAhead steps early.  With `dma`, the next
-  // tile's DMAs go out one every third MFMA, so their issue overlaps the
-  // MFMA pipe instead of stalling the wave in one burst.
-  __device__ __forceinline__ void pv(const char* K, const bf16x8_t (&p)[2],
-                                     f32x16_t (&o)[kLoraRank / 32],
-                                     const TileDma* dma = nullptr) const {
-    constexpr int kAhead = 3;
-    constexpr int kSteps = 2 * (kLoraRank / 32);
-    const char* kv0 = K + pv_off0;
-    const char* kv1 = K + pv_off1;
-    auto vload = [&](int st) {  // column block st % 16, key half st / 16
-      const int off = (st & 15) * 2048 + (st >> 4) * 256;
+  // O^T += V^T . P^T for the tile in stage V with the probabilities of every
+  // head slot in P buffer Pb: this wave's 32-column blocks
+  // [w kDimBlocks, (w+1) kDimBlocks) times each head group's P^T.
+  // Consecutive MFMAs go to different accumulators; V^T operands are read
+  // kAhead column blocks early.
+  __device__ __forceinline__ void pv(const char* V, f32x16_t (&o)[NW][kDimBlocks]) const {
+    const char* Pb = pbuf();
+    constexpr int kSteps = 2 * kDimBlocks;  // (key half, column block)
+    constexpr int kAhead = NW == 1 ? 4 : 2;
+    const char* kv0 = V + pv_off0 + wave * kDimBlocks * 2048;
+    const char* kv1 = V + pv_off1 + wave * kDimBlocks * 2048;
+    auto vload = [&](int st) {  // column block st % kDimBlocks, key half st / kDimBlocks
+      const int off = (st % kDimBlocks) * 2048 + (st / kDimBlocks) * 256;
       const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(kv0 + off));
       const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(kv1 + off));
       return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
+    auto pload = [&](int g, int ks) {
+      return *reinterpret_cast<const bf16x8_t*>(Pb + g * kPGroupBytes + ks * (kWave * 16) +
+                                                lane * 16);
+    };
+    bf16x8_t pb[NW], pn[NW];
+#pragma unroll
+    for (int g = 0; g < NW; ++g) pb[g] = pload(g, 0);
     bf16x8_t vbuf[kAhead];
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) vbuf[i] = vload(i);
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) {
-      const bf16x8_t v = vbuf[st % kAhead];
+      bf16x8_t v = vbuf[st % kAhead];
+      in_vgpr(v);  // (at the use: the asm waits for the load)
       if (st + kAhead < kSteps) vbuf[st % kAhead] = vload(st + kAhead);
-      o[st & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, p[st >> 4], o[st & 15], 0, 0, 0);
-      if (dma && (st % 3) == 2 && st / 3 < kLoadsPerWave) issue_one(*dma, st / 3);
-    }
-    if (dma) {  // waves of fewer than 4 per workgroup issue more DMAs per tile
+      const int db = st % kDimBlocks;
+      if (st == kDimBlocks / 2) {  // the second key half's P^T, half a pass early
 #pragma unroll
-      for (int j = kSteps / 3; j < kLoadsPerWave; ++j) issue_one(*dma, j);
+        for (int g = 0; g < NW; ++g) pn[g] = pload(g, 1);
+      }
+      if (st == kDimBlocks) {
+#pragma unroll
+        for (int g = 0; g < NW; ++g) pb[g] = pn[g];
+      }
+#pragma unroll
+      for (int g = 0; g < NW; ++g) {
+        bf16x8_t b = pb[g];
+        in_vgpr(b);
+        o[g][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, b, o[g][db], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
   // Writes the item's result.  The accumulators are never touched by VALU
   // code here (that makes the compiler shuttle all 256 of them through
-  // VGPRs): a partial piece stores the raw sums and 1/l for the merge kernel;
-  // a final item stages the raw sums through this wave's LDS region, then
-  // normalises, converts and stores 16 bytes per lane, 4 heads x 256 B
-  // contiguous per instruction.  The caller has made the LDS stages free.
-  __device__ __forceinline__ void finish(f32x16_t (&o)[kLoraRank / 32], float m_run,
+  // VGPRs).  Lane l holds, for head group g, head 32g + l%32 and columns
+  // 32 (w kDimBlocks + db) + 8 (j/4) + 4 (l/32) + j%4.  A partial piece
+  // stores the raw sums and 1/l for the merge kernel; a final item stages
+  // the raw sums through this wave's LDS region head group by head group,
+  // then normalises, converts and stores 16 bytes per lane.  The caller has
+  // made the LDS stages free.
+  __device__ __forceinline__ void finish(f32x16_t (&o)[NW][kDimBlocks], float m_ref,
                                          float l_run) const {
+    const int lane = opaque(this->lane);
+    const int l32 = lane & 31, half = lane >> 5;
+    const int head = wave * 32 + l32;
+    const bool head_ok = head < a.num_heads;
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const bool any = l_tot > 0.f;
     const float inv = any ? 1.f / l_tot : 0.f;
-    const float lse_v = any ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    const float lse_v = any ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
     const int H = a.num_heads;
+    const int col0 = wave * kDimBlocks * 32;
     if (slot >= 0) {
-      if (head_ok) {
-        float* dst = a.part_o + (static_cast<int64_t>(slot) * H + head) * kLoraRank;
+      if (head_ok && half == 0) {
+        const int64_t sh = static_cast<int64_t>(slot) * H + head;
+        a.part_lse[sh] = lse_v;
+        a.part_scale[sh] = inv;
+      }
 #pragma unroll
-        for (int mb = 0; mb < kLoraRank / 32; ++mb)
+      for (int g = 0; g < NW; ++g) {
+        const int hg = g * 32 + l32;
+        if (hg < H) {
+          float* dst = a.part_o + (static_cast<int64_t>(slot) * H + hg) * kLoraRank + col0;
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const f32x4_t w = {o[mb][4 * q4], o[mb][4 * q4 + 1], o[mb][4 * q4 + 2],
-                               o[mb][4 * q4 + 3]};
-            *reinterpret_cast<f32x4_t*>(dst + mb * 32 + q4 * 8 + half * 4) = w;
-          }
-        if (half == 0) {
-          const int64_t sh = static_cast<int64_t>(slot) * H + head;
-          a.part_lse[sh] = lse_v;
-          a.part_scale[sh] = inv;
+          for (int db = 0; db < kDimBlocks; ++db)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const f32x4_t w = {o[g][db][4 * q4], o[g][db][4 * q4 + 1], o[g][db][4 * q4 + 2],
+                                 o[g][db][4 * q4 + 3]};
+              *reinterpret_cast<f32x4_t*>(dst + db * 32 + q4 * 8 + half * 4) = w;
+            }
         }
       }
       return;
     }
-    float* R = reinterpret_cast<float*>(smem + wave * kFinishWaveBytes);
-    float* inv_h = R + 32 * kFinishRow;
-    if (half == 0) inv_h[l32] = inv;
+    float* X = reinterpret_cast<float*>(smem + kXchgOff);
+    if (half == 0) X[head] = inv;
     if (a.lse && head_ok && half == 0) a.lse[static_cast<int64_t>(token) * H + head] = lse_v;
+    lds_barrier();
+    float* R = reinterpret_cast<float*>(smem + wave * kFinWaveBytes);
+    constexpr int kChunks = kDimBlocks * 4;  // 8-column chunks per head row
 #pragma unroll
-    for (int round = 0; round < kLoraRank / 128; ++round) {
+    for (int g = 0; g < NW; ++g) {
 #pragma unroll
-      for (int m4 = 0; m4 < 4; ++m4) {
-        const int mb = round * 4 + m4;
+      for (int db = 0; db < kDimBlocks; ++db)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x4_t w = {o[mb][4 * q4], o[mb][4 * q4 + 1], o[mb][4 * q4 + 2],
-                             o[mb][4 * q4 + 3]};
-          *reinterpret_cast<f32x4_t*>(R + l32 * kFinishRow + m4 * 32 + q4 * 8 + half * 4) = w;
+          const f32x4_t w = {o[g][db][4 * q4], o[g][db][4 * q4 + 1], o[g][db][4 * q4 + 2],
+                             o[g][db][4 * q4 + 3]};
+          *reinterpret_cast<f32x4_t*>(R + l32 * kFinRow + db * 32 + q4 * 8 + half * 4) = w;
         }
-      }
-      // lane: head h = (lane + 64 r) / 16 of the wave, 8 columns cc * 8 of
-      // this round's 128.
+      // lane: head h = (lane + 64 r) / kChunks of the group, chunk cc.
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int qi = lane + 64 * r;
-        const int h = qi >> 4, cc = qi & 15;
-        const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(R + h * kFinishRow + cc * 8);
-        const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(R + h * kFinishRow + cc * 8 + 4);
-        const float sc = inv_h[h];
+      for (int r = 0; r < 32 * kChunks / kWave; ++r) {
+        const int qi = lane + kWave * r;
+        const int h = qi / kChunks, cc = qi % kChunks;
+        const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(R + h * kFinRow + cc * 8);
+        const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(R + h * kFinRow + cc * 8 + 4);
+        const int hg = g * 32 + h;
+        const float sc = X[hg];
         u32x4_t w;
         w[0] = f32_to_bf16_bits(v0[0] * sc) | (static_cast<unsigned>(f32_to_bf16_bits(v0[1] * sc)) << 16);
         w[1] = f32_to_bf16_bits(v0[2] * sc) | (static_cast<unsigned>(f32_to_bf16_bits(v0[3] * sc)) << 16);
         w[2] = f32_to_bf16_bits(v1[0] * sc) | (static_cast<unsigned>(f32_to_bf16_bits(v1[1] * sc)) << 16);
         w[3] = f32_to_bf16_bits(v1[2] * sc) | (static_cast<unsigned>(f32_to_bf16_bits(v1[3] * sc)) << 16);
-        const int hg = wave * 32 + h;
         if (hg < H)
           *reinterpret_cast<u32x4_t*>(a.out + (static_cast<int64_t>(token) * H + hg) * kLoraRank +
-                                      round * 128 + cc * 8) = w;
+                                      col0 + cc * 8) = w;
       }
     }
   }
@@ -569,8 +685,7 @@ struct Attn {
 template <int NW, bool kTileInPage>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attention_kernel(AttnArgs args) {
-  __shared__ __attribute__((aligned(1024)))
-  char smem[kStages * kTileBytes + kFlagBytes + kMaxItemPages * 4];
+  __shared__ __attribute__((aligned(1024))) char smem[Attn<NW, kTileInPage>::kLdsBytes];
   Attn<NW, kTileInPage> k(args, smem);
   k.run();
 }
@@ -590,13 +705,10 @@ hipError_t launch_nw(const AttnArgs& a, int num_workers, hipStream_t stream) {
 
 hipError_t launch_attention(const AttnArgs& a, int num_workers, hipStream_t stream) {
   if (num_workers <= 0) return hipSuccess;
-  switch ((a.num_heads + 31) / 32) {
-    case 1: return launch_nw<1>(a, num_workers, stream);
-    case 2: return launch_nw<2>(a, num_workers, stream);
-    case 3: return launch_nw<3>(a, num_workers, stream);
-    case 4: return launch_nw<4>(a, num_workers, stream);
-    default: return hipErrorInvalidValue;
-  }
+  if (a.num_heads <= 0 || a.num_heads > kMaxHeads) return hipErrorInvalidValue;
+  if (a.num_heads <= 32) return launch_nw<1>(a, num_workers, stream);
+  if (a.num_heads <= 64) return launch_nw<2>(a, num_workers, stream);
+  return launch_nw<4>(a, num_workers, stream);
 }
 
 }  // namespace mla

@@ -40,9 +40,6 @@ struct CostModel {
 };
 
 constexpr int kMinPieceTiles = 2;
-// Longest work item: the kernel stages an item's page ids (one per tile when
-// a tile never crosses a page) in a fixed LDS array of this many entries.
-constexpr int kMaxItemTiles = 1024;
 
 // Greedy contiguous fill of `budget` cost per worker.  Returns the number of
 // workers used (may exceed num_workers only if forced onto the last one,

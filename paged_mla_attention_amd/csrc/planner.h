@@ -19,6 +19,10 @@ constexpr int kLoraRank = 512;
 constexpr int kRopeDim = 64;
 constexpr int kLatentDim = kLoraRank + kRopeDim;
 constexpr int kMaxHeads = 128;
+// Longest work item in tiles.  The attention kernel stages an item's page
+// ids (at most one per tile when a tile never crosses a page) in a fixed LDS
+// array of this many entries.
+constexpr int kMaxItemTiles = 1024;
 
 struct WorkItem {
   int32_t token;     // query token (row of q_nope / out)
