@@ -165,6 +165,55 @@ def copy_calibration(nbytes=1 << 30, reps=5):
                       "reps": reps}), flush=True)
 
 
+def _rocpd_counter(db_dir, counter, name_part):
+    """Per-dispatch values of one counter for the kernels whose name contains
+    name_part, from a rocprofv3 --pmc output directory (rocpd database)."""
+    import glob
+    import sqlite3
+    dbs = glob.glob(os.path.join(db_dir, "**", "*.db"), recursive=True)
+    if not dbs:
+        raise SystemExit(f"no rocprofv3 database under {db_dir}")
+    per = {}
+    con = sqlite3.connect(dbs[0])
+    for name, did, cn, cv in con.execute(
+            "select name, dispatch_id, counter_name, counter_value from pmc_events"):
+        if cn == counter and name_part in name:
+            per[did] = per.get(did, 0.0) + cv
+    con.close()
+    return [per[k] for k in sorted(per)]
+
+
+def record_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    """Writes profiles/traffic.json: HBM bytes per mla_run of the decode
+    workload from the FETCH_SIZE and WRITE_SIZE counters (KiB per dispatch),
+    each scaled by what the same counter reads for a device copy of known size
+    (bench.py --copy-calibration).  Input: four rocprofv3 --pmc output
+    directories of `bench.py --no-prefill` and `bench.py --copy-calibration`."""
+    copy_bytes = float(1 << 30)
+    cf = _rocpd_counter(copy_fetch_dir, "FETCH_SIZE", "copy")
+    cw = _rocpd_counter(copy_write_dir, "WRITE_SIZE", "copy")
+    if not cf or not cw:
+        raise SystemExit("copy calibration kernel not found in the profiles")
+    f_scale = copy_bytes / (float(np.median(cf)) * 1024.0)
+    w_scale = copy_bytes / (float(np.median(cw)) * 1024.0)
+    out = {}
+    for kern in ("attention_kernel", "split_merge_kernel"):
+        fe = _rocpd_counter(fetch_dir, "FETCH_SIZE", kern)
+        wr = _rocpd_counter(write_dir, "WRITE_SIZE", kern)
+        if fe and wr:
+            out[kern] = {"fetch_bytes": float(np.median(fe)) * 1024.0 * f_scale,
+                         "write_bytes": float(np.median(wr)) * 1024.0 * w_scale}
+    total = sum(v["fetch_bytes"] + v["write_bytes"] for v in out.values())
+    doc = {"decode": {"source_hash": kernel_source_hash(), "bytes_per_launch": round(total),
+                      "per_kernel": out, "fetch_scale": f_scale, "write_scale": w_scale,
+                      "note": "FETCH_SIZE/WRITE_SIZE per dispatch (KiB) x copy-calibrated scale; "
+                              "one mla_run = attention_kernel + split_merge_kernel"}}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as fh:
+        json.dump(doc, fh, indent=1)
+    print(json.dumps(doc))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,9 +221,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run only the chunked-prefill workload (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--record-traffic", nargs=4, metavar="DIR",
+                    help="write profiles/traffic.json from rocprofv3 --pmc directories: "
+                         "decode FETCH_SIZE, decode WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(*args.record_traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -187,6 +244,13 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+
+    if args.prefill_only:
+        wp = W.chunked_prefill()
+        p_ms, p_run_ms, _ = run_steps(wp, max(3, args.steps // 5), args.warmup, copies=1)
+        print(f"[bench] prefill: {p_ms:.3f} ms/step, mla_run {p_run_ms:.3f} ms", file=sys.stderr,
+              flush=True)
         return
 
     w = W.decode_batch()

@@ -48,6 +48,9 @@
 //     the key loop makes the in-order vmcnt drain the DMA queue;
 //   * items covering a token's whole key range write bf16 output + LSE;
 //     pieces of a split token write fp32 partials that a merge kernel combines.
+#include <type_traits>
+#include <utility>
+
 #include "kernels.h"
 
 namespace mla {
@@ -69,6 +72,11 @@ constexpr int kStages = 4;
 constexpr int kStageBytes = kStages * kTileBytes;
 constexpr int kPGroupBytes = 2 * kWave * 16;      // one wave's P^T operands of a tile
 constexpr float kMaxExponent = 64.0f;             // log2 headroom above the reference
+// LDS layout of a tile: 16-byte chunk (key, dc) (dc = 8-column chunk of the
+// 576 latent columns) at (dc/2)*1024 + (dc%2)*512 + ((key ^ swz(dc))*16)
+// with swz(dc) = kSwzA*(dc%2) ^ kSwzB*((dc/2)%2).
+constexpr int kSwzA = 4;
+constexpr int kSwzB = 8;
 constexpr float kLn2 = 0.693147180559945309f;
 
 // s_waitcnt immediates (gfx9 encoding) that wait on one counter and leave
@@ -96,6 +104,17 @@ __device__ __forceinline__ void lds_barrier() {
 // output accumulators.  Applied where the operand is used (the asm waits for
 // a pending load of it).
 __device__ __forceinline__ void in_vgpr(bf16x8_t& v) { asm("" : "+v"(v)); }
+
+// f(integral_constant<int, I>) for I = 0 .. N-1, in order, fully unrolled
+// (the index is a compile-time constant in f).
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // A per-call copy of a lane value the compiler cannot see through: address
 // arithmetic derived from it stays where it is used instead of being hoisted
@@ -146,9 +165,9 @@ struct Attn {
     head = wave * 32 + l32;
     head_ok = head < a.num_heads;
     lds_base = static_cast<uint32_t>(reinterpret_cast<size_t>((__attribute__((address_space(3))) char*)smem));
-    // loader: lane p of DMA instruction I fetches key (p%32) ^ 4(p/32) ^ 8(I%2),
+    // loader: lane p of DMA instruction I fetches key (p%32) ^ swz(2I + p/32),
     // chunk 2I + p/32 (the XOR by 8 is folded in when the DMA is issued)
-    ld_key = l32 ^ (4 * half);
+    ld_key = l32 ^ (kSwzA * half);
     ld_off = half * 16;
     // score operand (16x16x32, A = K): lane (l16 = key in a 16-key block,
     // g4 = lane/16) reads chunk 4ks + g4 of key 16kb + l16 at
@@ -156,7 +175,7 @@ struct Attn {
     {
       const int l16 = lane & 15, g4 = lane >> 4;
       qk_off = (g4 >> 1) * 1024 + (g4 & 1) * 512 +
-               ((l16 ^ (4 * (g4 & 1)) ^ (8 * ((g4 >> 1) & 1))) * 16);
+               ((l16 ^ (kSwzA * (g4 & 1)) ^ (kSwzB * ((g4 >> 1) & 1))) * 16);
     }
     // P.V operand through the 16-lane transpose read: group G = lane/16 is
     // (key half g2, 16-column group cg); source lane s of the group points at
@@ -165,8 +184,9 @@ struct Attn {
     const int g2 = G >> 1, cg = G & 1;
     const int par = (sl >> 1) & 1;  // chunk parity of the source columns
     const int pv_base = cg * 1024 + par * 512 + (sl & 1) * 8;
-    pv_off0 = pv_base + ((8 * (g2 ^ cg) + 4 * (0 ^ par) + (sl >> 2)) * 16);
-    pv_off1 = pv_base + ((8 * (g2 ^ cg) + 4 * (1 ^ par) + (sl >> 2)) * 16);
+    const int swz = kSwzA * par ^ kSwzB * cg;
+    pv_off0 = pv_base + (((8 * g2 + (sl >> 2)) ^ swz) * 16);
+    pv_off1 = pv_base + (((8 * g2 + 4 + (sl >> 2)) ^ swz) * 16);
   }
 
   __device__ __forceinline__ char* pbuf() const { return smem + kStageBytes; }
@@ -250,7 +270,7 @@ struct Attn {
   __device__ __forceinline__ TileDma prep_tile(int t, int pg) const {
     const int P = a.page_size;
     const int base = kv_begin + t * kTileKeys;
-    int ke = base + ld_key, ko = base + (ld_key ^ 8);
+    int ke = base + ld_key, ko = base + (ld_key ^ kSwzB);
     ke = ke < kv_end ? ke : kv_end - 1;
     ko = ko < kv_end ? ko : kv_end - 1;
     TileDma d;
@@ -403,15 +423,28 @@ struct Attn {
           lds_barrier();
           const bool dma = t + kStages - 1 < ntiles;
           TileDma d;
-          if (dma) {
+          auto prep = [&] {
             d = prep_tile(t + kStages - 1, kTileInPage ? __builtin_amdgcn_readfirstlane(pg_next) : 0);
             if (kTileInPage) {  // the next tile's page id, read a tile ahead
               const int tn = t + kStages < ntiles ? t + kStages : ntiles - 1;
               pg_next = tile_page_v(tn);
             }
-          }
+          };
+          // With several waves, tile t+3's DMA set-up goes under the first
+          // k-step's MFMAs (a lone wave, with four times the DMAs, has no
+          // registers to spare there).  Its DMAs go under the other k-steps.
+          constexpr bool kPrepUnder = NW > 1;
+          if (!kPrepUnder && dma) prep();
           float x[2][8];
-          scores(stage(t), q, x, dma, d);
+          scores(stage(t), q, x, [&](auto kc) {
+            constexpr int k = decltype(kc)::value;
+            if (!dma) return;
+            if constexpr (k == 0) {
+              if (kPrepUnder) prep();
+            } else {
+              dma_step<k>(d);
+            }
+          });
           bf16x8_t p[2];
           softmax(x, kv_begin + t * kTileKeys, t == 0, m_ref, m_seen, l_run, p);
           store_p(p);
@@ -440,25 +473,23 @@ struct Attn {
       *reinterpret_cast<bf16x8_t*>(pb + wave * kPGroupBytes + ks * (kWave * 16) + lane * 16) = p[ks];
   }
 
-  // The DMAs of k-step ks (of 18) of a score pass, spread evenly.
-  template <int ks = 0>
-  __device__ __forceinline__ void dma_step_ct(const TileDma& d, int k) const {
-    if constexpr (ks < kQSteps) {
-      if (k == ks)
-        issue_range<ks * kLoadsPerWave / kQSteps, (ks + 1) * kLoadsPerWave / kQSteps>(d);
-      else
-        dma_step_ct<ks + 1>(d, k);
-    }
+  // The DMAs issued under k-step ks = 1 .. 17 of a score pass (k-step 0
+  // prepares them), spread evenly.
+  template <int ks>
+  __device__ __forceinline__ void dma_step(const TileDma& d) const {
+    static_assert(ks >= 1 && ks < kQSteps, "DMAs go under k-steps 1 .. 17");
+    constexpr int kN = kQSteps - 1;
+    issue_range<(ks - 1) * kLoadsPerWave / kN, ks * kLoadsPerWave / kN>(d);
   }
-  __device__ __forceinline__ void dma_step(const TileDma& d, int ks) const { dma_step_ct<0>(d, ks); }
 
   // S^T of the tile in stage K: four 16x16x32 accumulator chains
   // acc[kb][hb] (keys 16kb.., heads 16hb..), operands read kAhead k-steps
   // early; with dma a later tile's DMAs go out between the k-steps.  Then
   // the lane^16 exchange.  On return x[ks][e] is the score of key
   // 16ks + 8(lane/32) + e for head lane%32.
+  template <typename Extra>
   __device__ __forceinline__ void scores(const char* K, const u32x4_t (&q)[2][kQSteps],
-                                         float (&x)[2][8], bool dma, const TileDma& d) const {
+                                         float (&x)[2][8], Extra&& extra) const {
     constexpr int kAhead = 2;
     const char* kq = K + qk_off;
     auto kload = [&](int ks, int kb) {
@@ -475,12 +506,12 @@ struct Attn {
       kbuf[i][0] = kload(i, 0);
       kbuf[i][1] = kload(i, 1);
     }
-#pragma unroll
-    for (int ks = 0; ks < kQSteps; ++ks) {
+    static_for<kQSteps>([&](auto kc) {
+      constexpr int ks = decltype(kc)::value;
       bf16x8_t k0 = kbuf[ks % kAhead][0], k1 = kbuf[ks % kAhead][1];
       in_vgpr(k0);  // (at the use: the asm waits for the load)
       in_vgpr(k1);
-      if (ks + kAhead < kQSteps) {
+      if constexpr (ks + kAhead < kQSteps) {
         kbuf[ks % kAhead][0] = kload(ks + kAhead, 0);
         kbuf[ks % kAhead][1] = kload(ks + kAhead, 1);
       }
@@ -488,14 +519,14 @@ struct Attn {
       acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, __builtin_bit_cast(bf16x8_t, q[0][ks]), acc[1][0], 0, 0, 0);
       acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, __builtin_bit_cast(bf16x8_t, q[1][ks]), acc[0][1], 0, 0, 0);
       acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, __builtin_bit_cast(bf16x8_t, q[1][ks]), acc[1][1], 0, 0, 0);
-      if (dma) dma_step(d, ks);  // this k-step's share of the DMAs
+      extra(kc);  // work placed under this k-step's MFMAs
       // Keep each k-step's reads kAhead steps ahead instead of letting the
       // scheduler hoist all 36 (they would not fit in registers).
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
     // acc[kb][hb][i] is key 16kb + 4(lane/16) + i of head 16hb + lane%16.
-    // Lane l keeps head block hb_t = (l/16)%2 (its head l%32) and trades the
-    // other block with lane l^16, whose head it is.
+    // Lane l keeps head block (l/16)%2 (its head l%32) and trades the other
+    // block with lane l^16, whose head it is.
     const int g4 = lane >> 4;
     const bool odd = g4 & 1;
 #pragma unroll
@@ -505,8 +536,8 @@ struct Attn {
         const float own = odd ? acc[kb][1][i] : acc[kb][0][i];
         const float give = odd ? acc[kb][0][i] : acc[kb][1][i];
         const float got = __shfl_xor(give, 16);
-        x[kb][i] = odd ? got : own;      // keys 16kb + 8(l/32) + i
-        x[kb][4 + i] = odd ? own : got;  // keys 16kb + 8(l/32) + 4 + i
+        x[kb][i] = odd ? got : own;
+        x[kb][4 + i] = odd ? own : got;
       }
     }
   }
@@ -518,7 +549,7 @@ struct Attn {
   // (last tile only) get probability 0.
   __device__ __forceinline__ void softmax(float (&x)[2][8], int base, bool first, float& m_ref,
                                           float& m_seen, float& l_run, bf16x8_t (&p)[2]) const {
-    if (base + kTileKeys > kv_end) {
+    if (__builtin_expect(base + kTileKeys > kv_end, 0)) {  // the item's last tile only
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -538,13 +569,15 @@ struct Attn {
       const float mh = fmaxf(mx, __shfl_xor(mx, 32));
       if (m_ref == -INFINITY) m_ref = mh;  // O is still zero
     }
+    // No clamp against overflow: a score more than 2^64 above the reference
+    // makes the item redo with a new reference, so whatever an overflow
+    // leaves in the accumulators is discarded.
     const float neg_ref = -m_ref;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float v = __builtin_amdgcn_exp2f(
-            fminf(__builtin_fmaf(x[ks][e], a.scale_log2, neg_ref), kMaxExponent));
+        const float v = __builtin_amdgcn_exp2f(__builtin_fmaf(x[ks][e], a.scale_log2, neg_ref));
         l_run += v;
         p[ks][e] = static_cast<__bf16>(v);
       }
