@@ -28,15 +28,16 @@ struct TokenWork {
   int32_t tiles;    // ceil(visible / kTileKeys)
 };
 
-// Cost of one work item in units of one key tile (32 latent rows, 36 KiB).
-// Loading the query of all heads costs about four tiles at 128 heads; a
-// partial result (fp32 output of all heads, written once and read back by the
-// merge) costs about seven.
+// Cost of one work item in units of one key tile (32 latent rows, 36 KiB),
+// fitted to per-workgroup timings on MI355X: at 128 heads a tile costs about
+// 4.5K cycles and an item's fixed part (query load, pipeline fill and drain,
+// output) about 31K, i.e. seven tiles; writing a partial (fp32 output of all
+// heads) adds under one.
 struct CostModel {
   double item;
   double split;
   explicit CostModel(int heads)
-      : item(1.0 + 4.0 * heads / 128.0), split(1.0 + 7.0 * heads / 128.0) {}
+      : item(1.0 + 6.0 * heads / 128.0), split(0.25 + 0.75 * heads / 128.0) {}
 };
 
 constexpr int kMinPieceTiles = 2;
