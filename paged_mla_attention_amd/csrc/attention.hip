@@ -637,11 +637,10 @@ struct Attn {
   // Writes the item's result.  The accumulators are never touched by VALU
   // code here (that makes the compiler shuttle all 256 of them through
   // VGPRs).  Lane l holds, for head group g, head 32g + l%32 and columns
-  // 32 (w kDimBlocks + db) + 8 (j/4) + 4 (l/32) + j%4.  A partial piece
-  // stores the raw sums and 1/l for the merge kernel; a final item stages
-  // the raw sums through this wave's LDS region head group by head group,
-  // then normalises, converts and stores 16 bytes per lane.  The caller has
-  // made the LDS stages free.
+  // 32 (w kDimBlocks + db) + 8 (j/4) + 4 (l/32) + j%4.  The raw sums go
+  // through this wave's LDS region head group by head group; then each lane
+  // normalises (1/l of the head, from its owner wave through LDS), converts
+  // and stores 16 bytes.  The caller has made the LDS stages free.
   __device__ __forceinline__ void finish(f32x16_t (&o)[NW][kDimBlocks], float m_ref,
                                          float l_run) const {
     const int lane = opaque(this->lane);
@@ -654,32 +653,14 @@ struct Attn {
     const float lse_v = any ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
     const int H = a.num_heads;
     const int col0 = wave * kDimBlocks * 32;
-    if (slot >= 0) {
-      if (head_ok && half == 0) {
-        const int64_t sh = static_cast<int64_t>(slot) * H + head;
-        a.part_lse[sh] = lse_v;
-        a.part_scale[sh] = inv;
-      }
-#pragma unroll
-      for (int g = 0; g < NW; ++g) {
-        const int hg = g * 32 + l32;
-        if (hg < H) {
-          float* dst = a.part_o + (static_cast<int64_t>(slot) * H + hg) * kLoraRank + col0;
-#pragma unroll
-          for (int db = 0; db < kDimBlocks; ++db)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-              const f32x4_t w = {o[g][db][4 * q4], o[g][db][4 * q4 + 1], o[g][db][4 * q4 + 2],
-                                 o[g][db][4 * q4 + 3]};
-              *reinterpret_cast<f32x4_t*>(dst + db * 32 + q4 * 8 + half * 4) = w;
-            }
-        }
-      }
-      return;
-    }
+    // A final item writes the token's output and LSE; a piece of a split
+    // token writes the same normalised bf16 rows and LSE to its slot.
+    const int64_t row0 = static_cast<int64_t>(slot >= 0 ? slot : token) * H;
+    uint16_t* dst_o = (slot >= 0 ? a.part_o : a.out) + row0 * kLoraRank;
+    float* dst_lse = slot >= 0 ? a.part_lse + row0 : (a.lse ? a.lse + row0 : nullptr);
     float* X = reinterpret_cast<float*>(smem + kXchgOff);
     if (half == 0) X[head] = inv;
-    if (a.lse && head_ok && half == 0) a.lse[static_cast<int64_t>(token) * H + head] = lse_v;
+    if (dst_lse && head_ok && half == 0) dst_lse[head] = lse_v;
     lds_barrier();
     float* R = reinterpret_cast<float*>(smem + wave * kFinWaveBytes);
     constexpr int kChunks = kDimBlocks * 4;  // 8-column chunks per head row
@@ -708,8 +689,7 @@ struct Attn {
         w[2] = f32_to_bf16_bits(v1[0] * sc) | (static_cast<unsigned>(f32_to_bf16_bits(v1[1] * sc)) << 16);
         w[3] = f32_to_bf16_bits(v1[2] * sc) | (static_cast<unsigned>(f32_to_bf16_bits(v1[3] * sc)) << 16);
         if (hg < H)
-          *reinterpret_cast<u32x4_t*>(a.out + (static_cast<int64_t>(token) * H + hg) * kLoraRank +
-                                      col0 + cc * 8) = w;
+          *reinterpret_cast<u32x4_t*>(dst_o + static_cast<int64_t>(hg) * kLoraRank + col0 + cc * 8) = w;
       }
     }
   }

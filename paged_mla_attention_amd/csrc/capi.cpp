@@ -165,8 +165,9 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
     if (e != hipSuccess) return hip_fail(e, "hipHostMalloc");
     p->h_stage_cap = total;
   }
+  // Partials: bf16 output rows [slots, H, 512] then fp32 LSE [slots, H].
   const size_t part_floats =
-      static_cast<size_t>(s.num_slots) * p->num_heads * (mla::kLoraRank + 2);
+      static_cast<size_t>(s.num_slots) * p->num_heads * (mla::kLoraRank / 2 + 1);
   if (total > p->d_stage_cap || part_floats > p->part_cap) {
     // Buffers may still be read by enqueued kernels of an earlier plan.
     e = hipDeviceSynchronize();
@@ -230,9 +231,8 @@ mla_status mla_run(mla_plan_t p, const void* q_nope, const void* q_pe, const voi
   a.kv_cache = static_cast<const uint16_t*>(kv_cache);
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
-  a.part_o = p->d_part;
-  a.part_lse = p->d_part ? p->d_part + slots_h * mla::kLoraRank : nullptr;
-  a.part_scale = p->d_part ? a.part_lse + slots_h : nullptr;
+  a.part_o = reinterpret_cast<uint16_t*>(p->d_part);
+  a.part_lse = p->d_part ? p->d_part + slots_h * (mla::kLoraRank / 2) : nullptr;
   a.worker_indptr = reinterpret_cast<const int32_t*>(p->d_stage);
   a.items = reinterpret_cast<const mla::WorkItem*>(p->d_stage + p->off_items);
   a.kv_indptr = reinterpret_cast<const int32_t*>(p->d_stage + p->off_kv_indptr);
@@ -246,7 +246,6 @@ mla_status mla_run(mla_plan_t p, const void* q_nope, const void* q_pe, const voi
     mla::SplitMergeArgs m{};
     m.part_o = a.part_o;
     m.part_lse = a.part_lse;
-    m.part_scale = a.part_scale;
     m.merges = reinterpret_cast<const mla::MergeItem*>(p->d_stage + p->off_merges);
     m.out = a.out;
     m.lse = lse;

@@ -15,9 +15,8 @@ struct AttnArgs {
   const uint16_t* kv_cache;  // bf16 [pages, page_size, 576]
   uint16_t* out;             // bf16 [T, H, 512]
   float* lse;                // fp32 [T, H] or nullptr
-  float* part_o;             // fp32 [slots, H, 512], unnormalised sums
+  uint16_t* part_o;          // bf16 [slots, H, 512], normalised output of each piece
   float* part_lse;           // fp32 [slots, H], natural-log LSE of the piece
-  float* part_scale;         // fp32 [slots, H], 1 / (softmax denominator)
   const int32_t* worker_indptr;
   const WorkItem* items;
   const int32_t* kv_indptr;
@@ -28,9 +27,8 @@ struct AttnArgs {
 };
 
 struct SplitMergeArgs {
-  const float* part_o;
+  const uint16_t* part_o;
   const float* part_lse;
-  const float* part_scale;
   const MergeItem* merges;
   uint16_t* out;
   float* lse;

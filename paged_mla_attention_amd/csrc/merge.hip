@@ -24,9 +24,8 @@ __device__ __forceinline__ float bf16_hi(unsigned w) {
   return __builtin_bit_cast(float, w & 0xFFFF0000u);
 }
 
-// Split-KV partials -> final bf16 output + LSE.  A piece k holds its raw
-// weighted sum O_k (relative to its own reference maximum), 1 / l_k and its
-// LSE s_k, so its normalised output is O_k / l_k.  One block of 128 threads
+// Split-KV partials -> final bf16 output + LSE.  A piece k holds its
+// normalised output o_k (bf16) and its LSE s_k.  One block of 128 threads
 // per (merge entry, head); each thread owns 4 consecutive latent columns.
 __global__ __launch_bounds__(128) void split_merge_kernel(SplitMergeArgs a) {
   const int h = blockIdx.x;
@@ -43,8 +42,9 @@ __global__ __launch_bounds__(128) void split_merge_kernel(SplitMergeArgs a) {
       const int64_t sh = static_cast<int64_t>(m.first_slot + k) * H + h;
       const float s = a.part_lse[sh];
       const float w = (s == -INFINITY) ? 0.f : expf(s - M);
-      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(a.part_o + sh * kLoraRank + c);
-      acc += (w * a.part_scale[sh]) * v;
+      const u32x2_t r = *reinterpret_cast<const u32x2_t*>(a.part_o + sh * kLoraRank + c);
+      const f32x4_t v = {bf16_lo(r[0]), bf16_hi(r[0]), bf16_lo(r[1]), bf16_hi(r[1])};
+      acc += w * v;
       wsum += w;
     }
   }
