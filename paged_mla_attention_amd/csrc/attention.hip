@@ -674,22 +674,35 @@ struct Attn {
                              o[g][db][4 * q4 + 3]};
           *reinterpret_cast<f32x4_t*>(R + l32 * kFinRow + db * 32 + q4 * 8 + half * 4) = w;
         }
-      // lane: head h = (lane + 64 r) / kChunks of the group, chunk cc.
+      // lane: head h = (lane + 64 r) / kChunks of the group, chunk cc.  Reads
+      // go out in batches ahead of the conversions and stores.
+      constexpr int kIters = 32 * kChunks / kWave;
+      constexpr int kBatch = kIters < 8 ? kIters : 8;
 #pragma unroll
-      for (int r = 0; r < 32 * kChunks / kWave; ++r) {
-        const int qi = lane + kWave * r;
-        const int h = qi / kChunks, cc = qi % kChunks;
-        const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(R + h * kFinRow + cc * 8);
-        const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(R + h * kFinRow + cc * 8 + 4);
-        const int hg = g * 32 + h;
-        const float sc = X[hg];
-        u32x4_t w;
-        w[0] = f32_to_bf16_bits(v0[0] * sc) | (static_cast<unsigned>(f32_to_bf16_bits(v0[1] * sc)) << 16);
-        w[1] = f32_to_bf16_bits(v0[2] * sc) | (static_cast<unsigned>(f32_to_bf16_bits(v0[3] * sc)) << 16);
-        w[2] = f32_to_bf16_bits(v1[0] * sc) | (static_cast<unsigned>(f32_to_bf16_bits(v1[1] * sc)) << 16);
-        w[3] = f32_to_bf16_bits(v1[2] * sc) | (static_cast<unsigned>(f32_to_bf16_bits(v1[3] * sc)) << 16);
-        if (hg < H)
-          *reinterpret_cast<u32x4_t*>(dst_o + static_cast<int64_t>(hg) * kLoraRank + col0 + cc * 8) = w;
+      for (int r0 = 0; r0 < kIters; r0 += kBatch) {
+        f32x4_t v0[kBatch], v1[kBatch];
+        float sc[kBatch];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+          const int qi = lane + kWave * (r0 + b);
+          const int h = qi / kChunks, cc = qi % kChunks;
+          v0[b] = *reinterpret_cast<const f32x4_t*>(R + h * kFinRow + cc * 8);
+          v1[b] = *reinterpret_cast<const f32x4_t*>(R + h * kFinRow + cc * 8 + 4);
+          sc[b] = X[g * 32 + h];
+        }
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+          const int qi = lane + kWave * (r0 + b);
+          const int h = qi / kChunks, cc = qi % kChunks;
+          const int hg = g * 32 + h;
+          u32x4_t w;
+          w[0] = f32_to_bf16_bits(v0[b][0] * sc[b]) | (static_cast<unsigned>(f32_to_bf16_bits(v0[b][1] * sc[b])) << 16);
+          w[1] = f32_to_bf16_bits(v0[b][2] * sc[b]) | (static_cast<unsigned>(f32_to_bf16_bits(v0[b][3] * sc[b])) << 16);
+          w[2] = f32_to_bf16_bits(v1[b][0] * sc[b]) | (static_cast<unsigned>(f32_to_bf16_bits(v1[b][1] * sc[b])) << 16);
+          w[3] = f32_to_bf16_bits(v1[b][2] * sc[b]) | (static_cast<unsigned>(f32_to_bf16_bits(v1[b][3] * sc[b])) << 16);
+          if (hg < H)
+            *reinterpret_cast<u32x4_t*>(dst_o + static_cast<int64_t>(hg) * kLoraRank + col0 + cc * 8) = w;
+        }
       }
     }
   }
