@@ -18,36 +18,42 @@
 //     each wave's transposed V reads by NW (a wave issues one transposing
 //     LDS read per ~24 cycles, which bounded a split by heads);
 //   * keys are processed in tiles of 32.  A tile is copied from HBM straight
-//     into LDS by global_load_lds (no staging registers) into four 36 KiB
-//     stages, with explicit vmcnt waits and one bare s_barrier per tile;
+//     into LDS by global_load_lds (no staging registers): its ckv columns
+//     into one of four 32 KiB stages, its kpe columns (read by the scores
+//     only) into one of three 4 KiB slots, two tiles ahead of the one being
+//     computed, with explicit vmcnt waits and bare s_barriers.  DMA
+//     addresses step through the item's page list (staged in LDS) with no
+//     division per tile;
 //   * one swizzled LDS layout serves both products: 16-byte chunk (key, dc)
-//     (dc = 8-column chunk of the 576 latent columns) sits at
-//     (dc/2)*1024 + (dc%2)*512 + (key ^ 4*(dc%2) ^ 8*((dc/2)%2))*16, which
-//     the loader writes as 36 DMA instructions of 1 KiB and which keeps both
-//     read patterns free of bank conflicts;
-//   * S^T = K . Q^T on v_mfma_f32_16x16x32_bf16: four independent
-//     accumulator chains (2 key blocks x 2 head blocks of 16).  One exchange
-//     of half the scores with lane^16 leaves each lane with 16 scores of ONE
-//     head (lane l: head l%32, keys 16ks + 8(l/32) + e), already laid out as
-//     the P^T operand of the 32x32x16 MFMA;
+//     (dc = 8-column chunk of the latent columns) sits at
+//     (dc/2)*1024 + (dc%2)*512 + (key ^ 4*(dc%2) ^ 8*((dc/2)%2))*16 of its
+//     stage or slot, which the loader writes as 1 KiB DMA instructions and
+//     which keeps both read patterns free of bank conflicts;
+//   * S^T = K . Q^T as one chain of 36 v_mfma_f32_32x32x16_bf16 over the
+//     576 columns (keys as M, the wave's 32 heads as N).  Its accumulator
+//     layout gives lane l 16 scores of head l%32 (keys 8i + 4(l/32) + j),
+//     which is the P^T operand of the P . V MFMA once the V^T reads take
+//     the keys in the same order: no lane exchange;
 //   * O^T += V^T . P^T on v_mfma_f32_32x32x16_bf16 with latent columns as M
-//     and heads as N; V^T is read from the same K tile with
+//     and heads as N; V^T is read from the same stage with
 //     ds_read_b64_tr_b16, whose 16-lane transpose turns four 8-byte row
 //     pieces into one column each;
-//   * software pipeline: iteration t computes S(t), then the softmax of tile
-//     t (VALU) next to P . V of tile t-1 (MFMA), and publishes P(t) in one
-//     of two LDS buffers.  Tile t+2 is DMA'd during S(t);
+//   * software pipeline (several waves, tiles within pages): iteration t
+//     computes S(t), then P . V of tile t-1 with the softmax of S(t) placed
+//     between its MFMAs, and publishes P(t) in the other of two LDS
+//     buffers; one barrier per tile;
 //   * softmax in base 2 against a per-head reference maximum fixed at the
 //     item's first tile: p = 2^(x - m_ref) is exact for any reference (output
 //     and LSE are normalised with the same value), so the O accumulators are
 //     never rescaled inside the key loop.  A later score more than 2^64 above
 //     the reference (which would overflow) makes the workgroup redo the item
 //     with the largest score seen as the reference;
-//   * page ids come through scalar loads issued one tile ahead, and the
-//     query rows through asm loads with one explicit wait, so nothing inside
-//     the key loop makes the in-order vmcnt drain the DMA queue;
+//   * the query rows are loaded and waited for before the item's first DMA,
+//     and page ids come from LDS, so nothing inside the key loop makes the
+//     in-order vmcnt drain the DMA queue;
 //   * items covering a token's whole key range write bf16 output + LSE;
-//     pieces of a split token write fp32 partials that a merge kernel combines.
+//     pieces of a split token write normalised bf16 partials and their LSE,
+//     which a merge kernel combines.
 #include <type_traits>
 #include <utility>
 
@@ -60,16 +66,23 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef short s16x4_t __attribute__((vector_size(8)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __attribute__((address_space(4))) const int32_t const_i32_t;
 
 constexpr int kWave = 64;
-constexpr int kQSteps = kLatentDim / 32;          // 18 k-steps of 32 over 576
+constexpr int kQSteps = kLatentDim / 16;          // 36 k-steps of 16 over 576
 constexpr int kDmaPerTile = kLatentDim / 16;      // 36 x 1 KiB (two 16-B chunks x 32 keys)
-constexpr int kTileBytes = kDmaPerTile * 1024;    // 36864
-constexpr int kStages = 4;
-constexpr int kStageBytes = kStages * kTileBytes;
+constexpr int kCkvDmas = kLoraRank / 16;          // 32 of the 36 carry ckv columns
+constexpr int kCkvBytes = kCkvDmas * 1024;        // a tile's ckv part (32 KiB)
+constexpr int kKpeBytes = (kDmaPerTile - kCkvDmas) * 1024;  // its kpe part (4 KiB)
+constexpr int kStages = 4;                        // ckv stages
+constexpr int kKpeSlots = 3;                      // kpe slots (read by the scores only)
+constexpr int kStageBytes = kStages * kCkvBytes;
+constexpr int kKpeOff = kStageBytes;
+constexpr int kTilesAhead = 2;                    // tiles in flight beyond the current one
 constexpr int kPGroupBytes = 2 * kWave * 16;      // one wave's P^T operands of a tile
 constexpr float kMaxExponent = 64.0f;             // log2 headroom above the reference
 // LDS layout of a tile: 16-byte chunk (key, dc) (dc = 8-column chunk of the
@@ -83,10 +96,6 @@ constexpr float kLn2 = 0.693147180559945309f;
 // the others alone.
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 constexpr int kLgkmZero = 0xF | (0x7 << 4) | (0x3 << 14);
-
-__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
-  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
-}
 
 // Barrier without the memory fence of __syncthreads (which would wait for
 // every outstanding LDS DMA): this wave's LDS accesses have completed, then
@@ -104,6 +113,21 @@ __device__ __forceinline__ void lds_barrier() {
 // output accumulators.  Applied where the operand is used (the asm waits for
 // a pending load of it).
 __device__ __forceinline__ void in_vgpr(bf16x8_t& v) { asm("" : "+v"(v)); }
+
+// v_mfma_f32_32x32x16_bf16 with its accumulator in VGPRs.  The compiler
+// gives every MFMA of a function the AGPR form once the function needs
+// AGPRs (the output accumulators fill them), so the score chain is issued
+// here.  Back-to-back MFMAs into the same accumulator need no wait states;
+// mfma_settle provides those before other instructions read the result.
+__device__ __forceinline__ void mfma_v_first(f32x16_t& acc, const bf16x8_t& a, const u32x4_t& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v(f32x16_t& acc, const bf16x8_t& a, const u32x4_t& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_settle(f32x16_t& acc) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc));
+}
 
 // f(integral_constant<int, I>) for I = 0 .. N-1, in order, fully unrolled
 // (the index is a compile-time constant in f).
@@ -131,14 +155,16 @@ struct Attn {
   static constexpr int kLoadsPerWave = kDmaPerTile / NW;    // DMA instructions per tile per wave
   static_assert(kDmaPerTile % NW == 0 && (kLoraRank / 32) % NW == 0, "NW must be 1, 2 or 4");
   static_assert(kLoadsPerWave <= 63, "vmcnt holds at most 63");
-  static constexpr int kWaitTwo = 2 * kLoadsPerWave > 63 ? 63 : 2 * kLoadsPerWave;
   static constexpr int kPBufBytes = NW * kPGroupBytes;
-  static constexpr int kFlagOff = kStageBytes + kPBufBytes;  // per-wave redo flags
+  static constexpr int kPOff = kKpeOff + kKpeSlots * kKpeBytes;  // two P buffers
+  // Per-wave redo flags, in a kpe slot (used after the key loop only).
+  static constexpr int kFlagOff = kKpeOff;
   // Page ids of the current item (tiles that never span pages): an item has
   // at most kMaxItemTiles tiles, so at most that many pages.
-  static constexpr int kPageOff = kFlagOff + 16;
+  static constexpr int kPageOff = kPOff + 2 * kPBufBytes;
   static constexpr int kPageLoads = (kMaxItemTiles + NW * kWave - 1) / (NW * kWave);
   static constexpr int kLdsBytes = kPageOff + (kTileInPage ? kMaxItemTiles * 4 : 16);
+  static_assert(kLdsBytes <= 160 * 1024, "LDS holds 160 KiB");
   // Output staging in the idle stages: per wave, 32 head rows of its columns.
   static constexpr int kFinRow = kDimBlocks * 32 + 4;  // floats (padding staggers banks)
   static constexpr int kFinWaveBytes = 32 * kFinRow * 4;
@@ -149,7 +175,7 @@ struct Attn {
   char* smem;
   int lane, l32, half, wave, head;
   bool head_ok;
-  int ld_key, ld_off, qk_off, pv_off0, pv_off1;  // per-lane LDS / row offsets
+  int ld_key, ld_off, qk_off_e, qk_off_o, pv_off0, pv_off1;  // per-lane LDS / row offsets
   uint32_t lds_base;                               // LDS address of the stages
   // current item
   int token, kv_begin, kv_end, slot;
@@ -169,38 +195,40 @@ struct Attn {
     // chunk 2I + p/32 (the XOR by 8 is folded in when the DMA is issued)
     ld_key = l32 ^ (kSwzA * half);
     ld_off = half * 16;
-    // score operand (16x16x32, A = K): lane (l16 = key in a 16-key block,
-    // g4 = lane/16) reads chunk 4ks + g4 of key 16kb + l16 at
-    // ks*2048 + kb*256 + qk_off
-    {
-      const int l16 = lane & 15, g4 = lane >> 4;
-      qk_off = (g4 >> 1) * 1024 + (g4 & 1) * 512 +
-               ((l16 ^ (kSwzA * (g4 & 1)) ^ (kSwzB * ((g4 >> 1) & 1))) * 16);
-    }
+    // score operand (32x32x16, A = K): lane (key l32, dim half `half`)
+    // reads chunk 2ks + half of its key, at ks*1024 + qk_off_e (even ks) or
+    // qk_off_o (odd ks): one contiguous 256-byte run per 16 lanes.
+    qk_off_e = half * 512 + ((l32 ^ (kSwzA * half)) * 16);
+    qk_off_o = half * 512 + ((l32 ^ (kSwzA * half) ^ kSwzB) * 16);
     // P.V operand through the 16-lane transpose read: group G = lane/16 is
-    // (key half g2, 16-column group cg); source lane s of the group points at
-    // key 16ks + 8g2 + 4r + s/4 for read r (0, 1), columns 16cg + 4(s%4) .. +3.
+    // (key half g2, 16-column group cg).  MFMA k index 8 g2 + 4 r + j of key
+    // step kh holds key 16 kh + 8 r + 4 g2 + j (the order in which the score
+    // accumulators hold a lane's keys), so source lane s of the group points
+    // at key 16 kh + 8 r + 4 g2 + s/4 for read r (0, 1), columns
+    // 16 cg + 4 (s%4) .. +3.
     const int G = lane >> 4, sl = lane & 15;
     const int g2 = G >> 1, cg = G & 1;
     const int par = (sl >> 1) & 1;  // chunk parity of the source columns
     const int pv_base = cg * 1024 + par * 512 + (sl & 1) * 8;
     const int swz = kSwzA * par ^ kSwzB * cg;
-    pv_off0 = pv_base + (((8 * g2 + (sl >> 2)) ^ swz) * 16);
-    pv_off1 = pv_base + (((8 * g2 + 4 + (sl >> 2)) ^ swz) * 16);
+    pv_off0 = pv_base + (((4 * g2 + (sl >> 2)) ^ swz) * 16);
+    pv_off1 = pv_base + (((8 + 4 * g2 + (sl >> 2)) ^ swz) * 16);
   }
 
-  __device__ __forceinline__ char* pbuf() const { return smem + kStageBytes; }
+  __device__ __forceinline__ char* pbuf(int t) const { return smem + kPOff + (t & 1) * kPBufBytes; }
   __device__ __forceinline__ const char* stage(int t) const {
-    return smem + (t % kStages) * kTileBytes;
+    return smem + (t % kStages) * kCkvBytes;
+  }
+  __device__ __forceinline__ const char* kpe_slot(int t) const {
+    return smem + kKpeOff + (t % kKpeSlots) * kKpeBytes;
   }
 
-  // Page id of tile t of the item, from the item's page list in LDS (as a
-  // VGPR value; the caller makes it uniform where it uses it).  LDS reads
-  // keep the compiler's lgkmcnt waits exact, where a scalar load in flight
-  // would make every LDS wait a full drain.
-  __device__ __forceinline__ int tile_page_v(int t) const {
-    const int* pl = reinterpret_cast<const int*>(smem + kPageOff);
-    return pl[(kv_begin + t * kTileKeys) / a.page_size - first_page];
+  // Entry i of the item's page list in LDS (as a VGPR value; the caller
+  // makes it uniform where it uses it).  LDS reads keep the compiler's
+  // lgkmcnt waits exact, where a scalar load in flight would make every LDS
+  // wait a full drain.
+  __device__ __forceinline__ int page_at(int i) const {
+    return reinterpret_cast<const int*>(smem + kPageOff)[i];
   }
 
   // Page id for the lane's own key `key` of the tile starting at `base`
@@ -262,26 +290,31 @@ struct Attn {
     const char* sbase;  // tile in one page: page base (uniform) ...
     uint32_t voff_e;    // ... and the lane row offsets for even / odd I
     uint32_t voff_o;
-    uint32_t dst;       // LDS address of DMA I = wave
+    uint32_t dst;       // LDS address of DMA I = wave (ckv stage) ...
+    uint32_t dst2;      // ... and of I = wave + 32 (kpe slot), less 32 KiB
   };
 
-  // Tile t of the item; `pg` is the page of its first key (used when tiles
-  // never span pages).
-  __device__ __forceinline__ TileDma prep_tile(int t, int pg) const {
-    const int P = a.page_size;
+  // Tile t of the item.  When tiles never span pages, its keys are rows
+  // inp .. inp+31 of page pg (the caller steps through the page list, so
+  // no division by the page size happens per tile).
+  __device__ __forceinline__ TileDma prep_tile(int t, int pg, int inp) const {
     const int base = kv_begin + t * kTileKeys;
-    int ke = base + ld_key, ko = base + (ld_key ^ kSwzB);
-    ke = ke < kv_end ? ke : kv_end - 1;
-    ko = ko < kv_end ? ko : kv_end - 1;
     TileDma d;
-    d.dst = lds_base + (t % kStages) * kTileBytes + wave * 1024;
-    if (kTileInPage) {  // the tile lies in page pg: key k is row k - base + base % P
-      const int in_page = base % P;
-      d.sbase = reinterpret_cast<const char*>(a.kv_cache + static_cast<int64_t>(pg) * P * kLatentDim);
-      d.voff_e = static_cast<uint32_t>((in_page + ke - base) * (kLatentDim * 2) + ld_off + wave * 32);
-      d.voff_o = static_cast<uint32_t>((in_page + ko - base) * (kLatentDim * 2) + ld_off + wave * 32);
+    d.dst = lds_base + (t % kStages) * kCkvBytes + wave * 1024;
+    d.dst2 = lds_base + kKpeOff + (t % kKpeSlots) * kKpeBytes + wave * 1024 - kCkvBytes;
+    if (kTileInPage) {
+      const int rem = kv_end - 1 - base;  // keys past the item's end re-read its last key
+      const int lane_c = ld_off + wave * 32;
+      d.sbase = reinterpret_cast<const char*>(
+          a.kv_cache + static_cast<int64_t>(pg * a.page_size + inp) * kLatentDim);
+      d.voff_e = static_cast<uint32_t>(min(ld_key, rem) * (kLatentDim * 2) + lane_c);
+      d.voff_o = static_cast<uint32_t>(min(ld_key ^ kSwzB, rem) * (kLatentDim * 2) + lane_c);
       d.src_e = d.src_o = nullptr;
     } else {
+      const int P = a.page_size;
+      int ke = base + ld_key, ko = base + (ld_key ^ kSwzB);
+      ke = ke < kv_end ? ke : kv_end - 1;
+      ko = ko < kv_end ? ko : kv_end - 1;
       const int pe = lane_page(base, ke), po = lane_page(base, ko);
       d.src_e = reinterpret_cast<const char*>(
           a.kv_cache + (static_cast<int64_t>(pe) * P + ke % P) * kLatentDim) + ld_off + wave * 32;
@@ -300,7 +333,7 @@ struct Attn {
     constexpr int kOff = j * NW * 32;
     // The instruction offset moves the LDS destination as well as the
     // global address, so M0 takes it back off.
-    const uint32_t dst = d.dst + j * NW * 1024 - kOff;
+    const uint32_t dst = (j * NW < kCkvDmas ? d.dst : d.dst2) + j * NW * 1024 - kOff;
     const bool odd = NW == 1 ? (j & 1) : (wave & 1);
     if (kTileInPage)
       dma16s<kOff>(odd ? d.voff_o : d.voff_e, d.sbase, dst);
@@ -316,15 +349,14 @@ struct Attn {
     }
   }
 
-  __device__ __forceinline__ void issue_tile(int t, int pg) const {
-    const TileDma d = prep_tile(t, pg);
+  __device__ __forceinline__ void issue_tile(int t, int pg, int inp) const {
+    const TileDma d = prep_tile(t, pg, inp);
     issue_range<0, kLoadsPerWave>(d);
   }
 
-  // Waits for this wave's DMAs except those of the `later` newest tiles.
-  __device__ __forceinline__ static void wait_vm(int later) {
-    if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kWaitTwo));
-    else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerWave));
+  // Waits for this wave's DMAs except those of the newest tile if `later`.
+  __device__ __forceinline__ static void wait_vm(bool later) {
+    if (later) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerWave));
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   }
 
@@ -358,12 +390,34 @@ struct Attn {
         l_run = 0.f;
         m_seen = -INFINITY;
         if (ntiles == 0) break;
+        // Query as the B operand of the 32x32x16 score MFMAs: lane (l32,
+        // half) holds head 32 wave + l32, dims 16 ks + 8 half .. +8.  Padding
+        // heads (beyond H) compute with head 0's row; their results are never
+        // stored.  Loaded first (a redo attempt loads them again) and complete
+        // before the first DMA of the item, so that no wait for them can land
+        // in the key loop, where it would also wait for DMAs in flight.
+        u32x4_t q[kQSteps];
+        {
+          const int qlane = opaque(lane);
+          const int h = wave * 32 + (qlane & 31);
+          const int hq = h < H ? h : 0;
+          const uint16_t* qn = a.q_nope + (static_cast<int64_t>(token) * H + hq) * kLoraRank;
+          const uint16_t* qp = a.q_pe + (static_cast<int64_t>(token) * H + hq) * kRopeDim;
+          const int dl = 8 * (qlane >> 5);
+#pragma unroll
+          for (int ks = 0; ks < kQSteps; ++ks)
+            q[ks] = ks < kLoraRank / 16
+                        ? *reinterpret_cast<const u32x4_t*>(qn + ks * 16 + dl)
+                        : *reinterpret_cast<const u32x4_t*>(qp + (ks - kLoraRank / 16) * 16 + dl);
+        }
+        int n_pages = 1;
         if (kTileInPage) {
           // Stage the item's page ids in LDS; the loads go out before the
           // barrier that waits for the previous item's LDS users.
           const int P = a.page_size;
           first_page = kv_begin / P;
           const int n = (kv_end - 1) / P - first_page + 1;  // <= kMaxItemTiles
+          n_pages = n;
           int pv[kPageLoads];
 #pragma unroll
           for (int k = 0; k < kPageLoads; ++k) {
@@ -378,78 +432,101 @@ struct Attn {
             if (i < n) pl[i] = pv[k];
           }
         }
+        // The query rows have landed (the previous item's DMAs all have).
+#pragma unroll
+        for (int ks = 0; ks < kQSteps; ++ks) asm volatile("" : : "v"(q[ks]));
         // Every wave is done with the previous item's (or attempt's) LDS,
         // and the page list is complete.
         lds_barrier();
+        // Page-list cursor: entry and first row of the next tile to load.
+        int cur_pl = 0, cur_inp = kTileInPage ? kv_begin % a.page_size : 0;
+        auto advance = [&] {
+          cur_inp += kTileKeys;
+          if (cur_inp == a.page_size) {
+            cur_inp = 0;
+            ++cur_pl;
+          }
+        };
 #pragma unroll
-        for (int t = 0; t < kStages - 1; ++t)
-          if (t < ntiles)
-            issue_tile(t, kTileInPage ? __builtin_amdgcn_readfirstlane(tile_page_v(t)) : 0);
-        int pg_next = kTileInPage && ntiles > kStages - 1 ? tile_page_v(kStages - 1) : 0;
-        // Query as the B operand of the 16x16x32 score MFMAs: for head block
-        // hb, lane (l16, g4) holds head 32 wave + 16 hb + l16, dims
-        // 32 ks + 8 g4 .. +8.  Padding heads (beyond H) compute with head 0's
-        // row; their results are never stored.  Loaded after the first
-        // tiles' DMAs (the memory clobber keeps that order), so the
-        // compiler's waits for these loads also cover the DMAs before them.
-        asm volatile("" ::: "memory");
-        // (A redo attempt loads them again.)
-        u32x4_t q[2][kQSteps];
-        {
-          const int qlane = opaque(lane);
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb) {
-            const int h = wave * 32 + hb * 16 + (qlane & 15);
-            const int hq = h < H ? h : 0;
-            const uint16_t* qn = a.q_nope + (static_cast<int64_t>(token) * H + hq) * kLoraRank;
-            const uint16_t* qp = a.q_pe + (static_cast<int64_t>(token) * H + hq) * kRopeDim;
-            const int dl = 8 * (qlane >> 4);
-#pragma unroll
-            for (int ks = 0; ks < kQSteps; ++ks)
-              q[hb][ks] = ks < kLoraRank / 32
-                              ? *reinterpret_cast<const u32x4_t*>(qn + ks * 32 + dl)
-                              : *reinterpret_cast<const u32x4_t*>(qp + (ks - kLoraRank / 32) * 32 + dl);
+        for (int t = 0; t < kTilesAhead; ++t)
+          if (t < ntiles) {
+            issue_tile(t, kTileInPage ? __builtin_amdgcn_readfirstlane(page_at(cur_pl)) : 0, cur_inp);
+            if (kTileInPage) advance();
+          }
+        // The next tile's page id, read a tile ahead.
+        int pg_next = kTileInPage ? page_at(min(cur_pl, n_pages - 1)) : 0;
+        // Tile t: S(t), with the DMAs of tile t+2 between its k-steps; the
+        // softmax of S(t); P(t) published in LDS; this wave's columns of
+        // P(t) . V(t) for every head.  With several waves and tiles that
+        // never span pages, the tiles are software-pipelined: P . V of tile
+        // t-1 runs after S(t), with the softmax of S(t) placed between its
+        // MFMAs, and one barrier per tile serves both (tile t has landed,
+        // P(t-1) is complete, every wave is done with tile t-2's stage and
+        // tile t-1's kpe slot).  The other kernels (one wave, or tiles that
+        // span pages, whose DMA set-up takes more registers) keep the
+        // unpipelined order with a second barrier before P . V.
+        constexpr bool kPipe = kTileInPage && NW > 1;
+        for (int t = 0; t < ntiles; ++t) {
+          wait_vm(t + 1 < ntiles);
+          lds_barrier();
+          const bool dma = t + kTilesAhead < ntiles;
+          const int base = kv_begin + t * kTileKeys;
+          float x[16];
+          {
+            TileDma d;
+            auto prep = [&] {
+              d = prep_tile(t + kTilesAhead, kTileInPage ? __builtin_amdgcn_readfirstlane(pg_next) : 0,
+                            cur_inp);
+              if (kTileInPage) {
+                advance();
+                pg_next = page_at(min(cur_pl, n_pages - 1));
+              }
+            };
+            // With several waves, the DMA set-up goes under the first
+            // k-step's MFMA (a lone wave, with four times the DMAs, has no
+            // registers to spare there).  The DMAs go under the other
+            // k-steps.
+            constexpr bool kPrepUnder = NW > 1;
+            if (!kPrepUnder && dma) prep();
+            scores(stage(t), kpe_slot(t), q, x, [&](auto kc) {
+              constexpr int k = decltype(kc)::value;
+              if (!dma) return;
+              if constexpr (k == 0) {
+                if (kPrepUnder) prep();
+              } else {
+                dma_step<k>(d);
+              }
+            });
+          }
+          bf16x8_t p[2];
+          if (!kPipe || t == 0) {
+            const float mx = softmax_max(x, base, m_seen);
+            if (t == 0) {
+              const float mh = fmaxf(mx, __shfl_xor(mx, 32));
+              if (m_ref == -INFINITY) m_ref = mh;  // O is still zero
+            }
+            softmax_exp<0, 16>(x, -m_ref, l_run, p);
+          } else {
+            const float neg_ref = -m_ref;
+            pv(stage(t - 1), pbuf(t - 1), o, [&](auto sc) {
+              constexpr int st = decltype(sc)::value;
+              constexpr int kN = 2 * kDimBlocks - 1;  // P . V steps after the first
+              if constexpr (st == 0) {
+                softmax_max(x, base, m_seen);
+              } else {
+                softmax_exp<(st - 1) * 16 / kN, st * 16 / kN>(x, neg_ref, l_run, p);
+              }
+            });
+          }
+          store_p(p, pbuf(t));
+          if (!kPipe) {
+            lds_barrier();
+            pv(stage(t), pbuf(t), o, [&](auto) {});
           }
         }
-        // Tile t: S(t) (with the DMAs of tile t+3 in between), softmax,
-        // P(t) published in LDS, then this wave's columns of P . V for every
-        // head.  Barriers: tile t landed for every wave and P . V of t-1
-        // done (its stage and the P buffer are free); P(t) complete.  One
-        // loop body for every tile (uniform branches for the first tile, the
-        // DMAs and the partial last tile) keeps the code and its register
-        // allocation single.
-        for (int t = 0; t < ntiles; ++t) {
-          wait_vm(ntiles - 1 - t);
+        if (kPipe) {
           lds_barrier();
-          const bool dma = t + kStages - 1 < ntiles;
-          TileDma d;
-          auto prep = [&] {
-            d = prep_tile(t + kStages - 1, kTileInPage ? __builtin_amdgcn_readfirstlane(pg_next) : 0);
-            if (kTileInPage) {  // the next tile's page id, read a tile ahead
-              const int tn = t + kStages < ntiles ? t + kStages : ntiles - 1;
-              pg_next = tile_page_v(tn);
-            }
-          };
-          // With several waves, tile t+3's DMA set-up goes under the first
-          // k-step's MFMAs (a lone wave, with four times the DMAs, has no
-          // registers to spare there).  Its DMAs go under the other k-steps.
-          constexpr bool kPrepUnder = NW > 1;
-          if (!kPrepUnder && dma) prep();
-          float x[2][8];
-          scores(stage(t), q, x, [&](auto kc) {
-            constexpr int k = decltype(kc)::value;
-            if (!dma) return;
-            if constexpr (k == 0) {
-              if (kPrepUnder) prep();
-            } else {
-              dma_step<k>(d);
-            }
-          });
-          bf16x8_t p[2];
-          softmax(x, kv_begin + t * kTileKeys, t == 0, m_ref, m_seen, l_run, p);
-          store_p(p);
-          lds_barrier();
-          pv(stage(t), o);
+          pv(stage(ntiles - 1), pbuf(ntiles - 1), o, [&](auto) {});
         }
         // Redo the item if any head of the workgroup overflowed its reference.
         int* flags = reinterpret_cast<int*>(smem + kFlagOff);
@@ -466,121 +543,98 @@ struct Attn {
     }
   }
 
-  __device__ __forceinline__ void store_p(const bf16x8_t (&p)[2]) const {
-    char* pb = pbuf();
+  __device__ __forceinline__ void store_p(const bf16x8_t (&p)[2], char* pb) const {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
       *reinterpret_cast<bf16x8_t*>(pb + wave * kPGroupBytes + ks * (kWave * 16) + lane * 16) = p[ks];
   }
 
-  // The DMAs issued under k-step ks = 1 .. 17 of a score pass (k-step 0
+  // The DMAs issued under k-step ks = 1 .. 35 of a score pass (k-step 0
   // prepares them), spread evenly.
   template <int ks>
   __device__ __forceinline__ void dma_step(const TileDma& d) const {
-    static_assert(ks >= 1 && ks < kQSteps, "DMAs go under k-steps 1 .. 17");
+    static_assert(ks >= 1 && ks < kQSteps, "DMAs go under k-steps 1 .. 35");
     constexpr int kN = kQSteps - 1;
     issue_range<(ks - 1) * kLoadsPerWave / kN, ks * kLoadsPerWave / kN>(d);
   }
 
-  // S^T of the tile in stage K: four 16x16x32 accumulator chains
-  // acc[kb][hb] (keys 16kb.., heads 16hb..), operands read kAhead k-steps
-  // early; with dma a later tile's DMAs go out between the k-steps.  Then
-  // the lane^16 exchange.  On return x[ks][e] is the score of key
-  // 16ks + 8(lane/32) + e for head lane%32.
+  // S^T of the tile in stage K / kpe slot Kpe (keys x this wave's 32
+  // heads) as one chain of
+  // 36 v_mfma_f32_32x32x16_bf16 over the 576 latent columns, K operands read
+  // kAhead k-steps early; a later tile's DMAs go out between the k-steps.
+  // On return x[4 i + j] is the score of key 8 i + 4 (lane/32) + j for head
+  // lane%32: the accumulator layout, which the P . V step consumes as is.
   template <typename Extra>
-  __device__ __forceinline__ void scores(const char* K, const u32x4_t (&q)[2][kQSteps],
-                                         float (&x)[2][8], Extra&& extra) const {
-    constexpr int kAhead = 2;
-    const char* kq = K + qk_off;
-    auto kload = [&](int ks, int kb) {
-      return *reinterpret_cast<const bf16x8_t*>(kq + ks * 2048 + kb * 256);
+  __device__ __forceinline__ void scores(const char* K, const char* Kpe, const u32x4_t (&q)[kQSteps],
+                                         float (&x)[16], Extra&& extra) const {
+    constexpr int kAhead = 3;
+    const char* ke = K + qk_off_e;
+    const char* ko = K + qk_off_o;
+    const char* pe = Kpe + qk_off_e - kCkvBytes;
+    const char* po = Kpe + qk_off_o - kCkvBytes;
+    auto kload = [&](int ks) {  // k-steps 32 .. 35 (the kpe columns) from the kpe slot
+      const char* b = ks < kCkvDmas ? (ks & 1 ? ko : ke) : (ks & 1 ? po : pe);
+      return *reinterpret_cast<const bf16x8_t*>(b + ks * 1024);
     };
-    f32x4_t acc[2][2];
+    f32x16_t acc;
+    bf16x8_t kbuf[kAhead];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) acc[kb][hb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    bf16x8_t kbuf[kAhead][2];
-#pragma unroll
-    for (int i = 0; i < kAhead; ++i) {
-      kbuf[i][0] = kload(i, 0);
-      kbuf[i][1] = kload(i, 1);
-    }
+    for (int i = 0; i < kAhead; ++i) kbuf[i] = kload(i);
     static_for<kQSteps>([&](auto kc) {
       constexpr int ks = decltype(kc)::value;
-      bf16x8_t k0 = kbuf[ks % kAhead][0], k1 = kbuf[ks % kAhead][1];
+      bf16x8_t k0 = kbuf[ks % kAhead];
       in_vgpr(k0);  // (at the use: the asm waits for the load)
-      in_vgpr(k1);
-      if constexpr (ks + kAhead < kQSteps) {
-        kbuf[ks % kAhead][0] = kload(ks + kAhead, 0);
-        kbuf[ks % kAhead][1] = kload(ks + kAhead, 1);
-      }
-      acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, __builtin_bit_cast(bf16x8_t, q[0][ks]), acc[0][0], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, __builtin_bit_cast(bf16x8_t, q[0][ks]), acc[1][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, __builtin_bit_cast(bf16x8_t, q[1][ks]), acc[0][1], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, __builtin_bit_cast(bf16x8_t, q[1][ks]), acc[1][1], 0, 0, 0);
-      extra(kc);  // work placed under this k-step's MFMAs
-      // Keep each k-step's reads kAhead steps ahead instead of letting the
+      if constexpr (ks + kAhead < kQSteps) kbuf[ks % kAhead] = kload(ks + kAhead);
+      if constexpr (ks == 0)
+        mfma_v_first(acc, k0, q[ks]);
+      else
+        mfma_v(acc, k0, q[ks]);
+      extra(kc);  // work placed under this k-step's MFMA
+      // Keep each k-step's read kAhead steps ahead instead of letting the
       // scheduler hoist all 36 (they would not fit in registers).
       __builtin_amdgcn_sched_barrier(0);
     });
-    // acc[kb][hb][i] is key 16kb + 4(lane/16) + i of head 16hb + lane%16.
-    // Lane l keeps head block (l/16)%2 (its head l%32) and trades the other
-    // block with lane l^16, whose head it is.
-    const int g4 = lane >> 4;
-    const bool odd = g4 & 1;
+    mfma_settle(acc);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float own = odd ? acc[kb][1][i] : acc[kb][0][i];
-        const float give = odd ? acc[kb][0][i] : acc[kb][1][i];
-        const float got = __shfl_xor(give, 16);
-        x[kb][i] = odd ? got : own;
-        x[kb][4 + i] = odd ? own : got;
-      }
-    }
+    for (int j = 0; j < 16; ++j) x[j] = acc[j];
   }
 
-  // Softmax of one tile's scores against the item's reference maximum:
-  // p = 2^(s * scale_log2 - m_ref) as the bf16 P^T operand (x[ks][e] is key
-  // 16ks + 8 half + e of the lane's head).  The first tile of an attempt
-  // fixes the reference (unless a redo has set it); keys past the item's end
-  // (last tile only) get probability 0.
-  __device__ __forceinline__ void softmax(float (&x)[2][8], int base, bool first, float& m_ref,
-                                          float& m_seen, float& l_run, bf16x8_t (&p)[2]) const {
+  // Softmax of one tile's scores against the item's reference maximum,
+  // p = 2^(s * scale_log2 - m_ref), in pieces that the pipeline spreads
+  // between MFMAs.  x[4 i + j] is key 8 i + 4 half + j of the lane's head.
+  //
+  // softmax_max: keys past the item's end (last tile only) get score -inf;
+  // returns the lane's largest scaled score and folds it into m_seen.
+  __device__ __forceinline__ float softmax_max(float (&x)[16], int base, float& m_seen) const {
     if (__builtin_expect(base + kTileKeys > kv_end, 0)) {  // the item's last tile only
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int key = base + 16 * ks + 8 * half + e;
-          x[ks][e] = key < kv_end ? x[ks][e] : -INFINITY;
-        }
+      for (int j = 0; j < 16; ++j) {
+        const int key = base + 8 * (j >> 2) + 4 * half + (j & 3);
+        x[j] = key < kv_end ? x[j] : -INFINITY;
+      }
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, x[ks][e]);
+    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, x[j]);
     mx *= a.scale_log2;
     m_seen = fmaxf(m_seen, mx);
-    if (first) {
-      const float mh = fmaxf(mx, __shfl_xor(mx, 32));
-      if (m_ref == -INFINITY) m_ref = mh;  // O is still zero
+    return mx;
+  }
+
+  // softmax_exp: probabilities of x[j0 .. j1) as bf16 P^T operands
+  // (p[kh][e] = x[8 kh + e]) and their sum.  No clamp against overflow: a
+  // score more than 2^64 above the reference makes the item redo with a new
+  // reference, so whatever an overflow leaves in the accumulators is
+  // discarded.
+  template <int j0, int j1>
+  __device__ __forceinline__ void softmax_exp(const float (&x)[16], float neg_ref, float& l_run,
+                                              bf16x8_t (&p)[2]) const {
+#pragma unroll
+    for (int j = j0; j < j1; ++j) {
+      const float v = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], a.scale_log2, neg_ref));
+      l_run += v;
+      p[j >> 3][j & 7] = static_cast<__bf16>(v);
     }
-    // No clamp against overflow: a score more than 2^64 above the reference
-    // makes the item redo with a new reference, so whatever an overflow
-    // leaves in the accumulators is discarded.
-    const float neg_ref = -m_ref;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v = __builtin_amdgcn_exp2f(__builtin_fmaf(x[ks][e], a.scale_log2, neg_ref));
-        l_run += v;
-        p[ks][e] = static_cast<__bf16>(v);
-      }
   }
 
   // O^T += V^T . P^T for the tile in stage V with the probabilities of every
@@ -588,10 +642,11 @@ struct Attn {
   // [w kDimBlocks, (w+1) kDimBlocks) times each head group's P^T.
   // Consecutive MFMAs go to different accumulators; V^T operands are read
   // kAhead column blocks early.
-  __device__ __forceinline__ void pv(const char* V, f32x16_t (&o)[NW][kDimBlocks]) const {
-    const char* Pb = pbuf();
+  template <typename Extra>
+  __device__ __forceinline__ void pv(const char* V, const char* Pb, f32x16_t (&o)[NW][kDimBlocks],
+                                     Extra&& extra) const {
     constexpr int kSteps = 2 * kDimBlocks;  // (key half, column block)
-    constexpr int kAhead = NW == 1 ? 4 : 2;
+    constexpr int kAhead = 2;
     const char* kv0 = V + pv_off0 + wave * kDimBlocks * 2048;
     const char* kv1 = V + pv_off1 + wave * kDimBlocks * 2048;
     auto vload = [&](int st) {  // column block st % kDimBlocks, key half st / kDimBlocks
@@ -604,43 +659,40 @@ struct Attn {
       return *reinterpret_cast<const bf16x8_t*>(Pb + g * kPGroupBytes + ks * (kWave * 16) +
                                                 lane * 16);
     };
-    bf16x8_t pb[NW], pn[NW];
+    bf16x8_t pb[NW];
 #pragma unroll
     for (int g = 0; g < NW; ++g) pb[g] = pload(g, 0);
     bf16x8_t vbuf[kAhead];
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) vbuf[i] = vload(i);
-#pragma unroll
-    for (int st = 0; st < kSteps; ++st) {
+    static_for<kSteps>([&](auto sc) {
+      constexpr int st = decltype(sc)::value;
       bf16x8_t v = vbuf[st % kAhead];
       in_vgpr(v);  // (at the use: the asm waits for the load)
-      if (st + kAhead < kSteps) vbuf[st % kAhead] = vload(st + kAhead);
+      if constexpr (st + kAhead < kSteps) vbuf[st % kAhead] = vload(st + kAhead);
       const int db = st % kDimBlocks;
-      if (st == kDimBlocks / 2) {  // the second key half's P^T, half a pass early
-#pragma unroll
-        for (int g = 0; g < NW; ++g) pn[g] = pload(g, 1);
-      }
-      if (st == kDimBlocks) {
-#pragma unroll
-        for (int g = 0; g < NW; ++g) pb[g] = pn[g];
-      }
 #pragma unroll
       for (int g = 0; g < NW; ++g) {
         bf16x8_t b = pb[g];
         in_vgpr(b);
         o[g][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, b, o[g][db], 0, 0, 0);
+        // After its last use for the first key half, the group's operand
+        // register takes the second half's (a pass of MFMAs ahead of use).
+        if (st == kDimBlocks - 1) pb[g] = pload(g, 1);
       }
+      extra(sc);  // work placed under this step's MFMAs
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
   }
 
   // Writes the item's result.  The accumulators are never touched by VALU
   // code here (that makes the compiler shuttle all 256 of them through
   // VGPRs).  Lane l holds, for head group g, head 32g + l%32 and columns
   // 32 (w kDimBlocks + db) + 8 (j/4) + 4 (l/32) + j%4.  The raw sums go
-  // through this wave's LDS region head group by head group; then each lane
-  // normalises (1/l of the head, from its owner wave through LDS), converts
-  // and stores 16 bytes.  The caller has made the LDS stages free.
+  // through this wave's LDS region head group by head group (stored straight
+  // from the AGPRs); then each lane normalises 8 columns of one head (1/l of
+  // the head, from its owner wave through LDS), converts them and stores 16
+  // bytes.  The caller has made the LDS stages free.
   __device__ __forceinline__ void finish(f32x16_t (&o)[NW][kDimBlocks], float m_ref,
                                          float l_run) const {
     const int lane = opaque(this->lane);
@@ -652,59 +704,72 @@ struct Attn {
     const float inv = any ? 1.f / l_tot : 0.f;
     const float lse_v = any ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
     const int H = a.num_heads;
-    const int col0 = wave * kDimBlocks * 32;
     // A final item writes the token's output and LSE; a piece of a split
     // token writes the same normalised bf16 rows and LSE to its slot.
     const int64_t row0 = static_cast<int64_t>(slot >= 0 ? slot : token) * H;
-    uint16_t* dst_o = (slot >= 0 ? a.part_o : a.out) + row0 * kLoraRank;
+    uint16_t* dst_o = (slot >= 0 ? a.part_o : a.out) + row0 * kLoraRank + wave * kDimBlocks * 32;
     float* dst_lse = slot >= 0 ? a.part_lse + row0 : (a.lse ? a.lse + row0 : nullptr);
     float* X = reinterpret_cast<float*>(smem + kXchgOff);
     if (half == 0) X[head] = inv;
     if (dst_lse && head_ok && half == 0) dst_lse[head] = lse_v;
     lds_barrier();
     float* R = reinterpret_cast<float*>(smem + wave * kFinWaveBytes);
-    constexpr int kChunks = kDimBlocks * 4;  // 8-column chunks per head row
+    // Read-back task of lane: head hb + kHStep r of the group, 8-column chunk cc.
+    constexpr int kChunks = kDimBlocks * 4;  // 8-column chunks per head row (16, 32 or 64)
+    constexpr int kHStep = kWave / kChunks;  // heads per read-back round
+    constexpr int kRounds = 32 / kHStep;
+    const int hb = lane / kChunks, cc = lane % kChunks;
+    const float* rsrc = R + hb * kFinRow + cc * 8;
+    const float* xsrc = X + hb;
+    char* obase = reinterpret_cast<char*>(dst_o);
+    const uint32_t ooff = static_cast<uint32_t>((hb * kLoraRank + cc * 8) * 2);
+    // Padding head slots (H not a multiple of 32) are not stored.
+    auto write_out = [&](auto masked_c) {
+      constexpr bool kMasked = decltype(masked_c)::value;
 #pragma unroll
-    for (int g = 0; g < NW; ++g) {
+      for (int g = 0; g < NW; ++g) {
 #pragma unroll
-      for (int db = 0; db < kDimBlocks; ++db)
+        for (int db = 0; db < kDimBlocks; ++db)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x4_t w = {o[g][db][4 * q4], o[g][db][4 * q4 + 1], o[g][db][4 * q4 + 2],
-                             o[g][db][4 * q4 + 3]};
-          *reinterpret_cast<f32x4_t*>(R + l32 * kFinRow + db * 32 + q4 * 8 + half * 4) = w;
-        }
-      // lane: head h = (lane + 64 r) / kChunks of the group, chunk cc.  Reads
-      // go out in batches ahead of the conversions and stores.
-      constexpr int kIters = 32 * kChunks / kWave;
-      constexpr int kBatch = kIters < 8 ? kIters : 8;
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4_t w = {o[g][db][4 * q4], o[g][db][4 * q4 + 1], o[g][db][4 * q4 + 2],
+                               o[g][db][4 * q4 + 3]};
+            *reinterpret_cast<f32x4_t*>(R + l32 * kFinRow + db * 32 + q4 * 8 + half * 4) = w;
+          }
+        // Reads go out in batches ahead of the conversions and stores.
+        constexpr int kBatch = kRounds < 8 ? kRounds : 8;
 #pragma unroll
-      for (int r0 = 0; r0 < kIters; r0 += kBatch) {
-        f32x4_t v0[kBatch], v1[kBatch];
-        float sc[kBatch];
+        for (int r0 = 0; r0 < kRounds; r0 += kBatch) {
+          f32x4_t v0[kBatch], v1[kBatch];
+          float sc[kBatch];
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-          const int qi = lane + kWave * (r0 + b);
-          const int h = qi / kChunks, cc = qi % kChunks;
-          v0[b] = *reinterpret_cast<const f32x4_t*>(R + h * kFinRow + cc * 8);
-          v1[b] = *reinterpret_cast<const f32x4_t*>(R + h * kFinRow + cc * 8 + 4);
-          sc[b] = X[g * 32 + h];
-        }
+          for (int b = 0; b < kBatch; ++b) {
+            const float* src = rsrc + kHStep * (r0 + b) * kFinRow;
+            v0[b] = *reinterpret_cast<const f32x4_t*>(src);
+            v1[b] = *reinterpret_cast<const f32x4_t*>(src + 4);
+            sc[b] = xsrc[g * 32 + kHStep * (r0 + b)];
+          }
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-          const int qi = lane + kWave * (r0 + b);
-          const int h = qi / kChunks, cc = qi % kChunks;
-          const int hg = g * 32 + h;
-          u32x4_t w;
-          w[0] = f32_to_bf16_bits(v0[b][0] * sc[b]) | (static_cast<unsigned>(f32_to_bf16_bits(v0[b][1] * sc[b])) << 16);
-          w[1] = f32_to_bf16_bits(v0[b][2] * sc[b]) | (static_cast<unsigned>(f32_to_bf16_bits(v0[b][3] * sc[b])) << 16);
-          w[2] = f32_to_bf16_bits(v1[b][0] * sc[b]) | (static_cast<unsigned>(f32_to_bf16_bits(v1[b][1] * sc[b])) << 16);
-          w[3] = f32_to_bf16_bits(v1[b][2] * sc[b]) | (static_cast<unsigned>(f32_to_bf16_bits(v1[b][3] * sc[b])) << 16);
-          if (hg < H)
-            *reinterpret_cast<u32x4_t*>(dst_o + static_cast<int64_t>(hg) * kLoraRank + col0 + cc * 8) = w;
+          for (int b = 0; b < kBatch; ++b) {
+            const int hrel = g * 32 + kHStep * (r0 + b);  // head of the task, less hb
+            u32x4_t w;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const f32x2_t lo = {v0[b][2 * e] * sc[b], v0[b][2 * e + 1] * sc[b]};
+              const f32x2_t hi = {v1[b][2 * e] * sc[b], v1[b][2 * e + 1] * sc[b]};
+              w[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_t));
+              w[2 + e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t));
+            }
+            if (!kMasked || hb + hrel < H)
+              *reinterpret_cast<u32x4_t*>(obase + (ooff + hrel * kLoraRank * 2)) = w;
+          }
         }
       }
-    }
+    };
+    if (H >= NW * 32)
+      write_out(std::false_type{});
+    else
+      write_out(std::true_type{});
   }
 };
 
