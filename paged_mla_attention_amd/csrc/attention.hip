@@ -249,33 +249,30 @@ struct Attn {
   }
 
   // One 16-byte-per-lane DMA from global memory into LDS at
-  // m0 + offset + 16 * lane:
-  // lane row address (64-bit VGPR pair, `off` form) or a uniform base (SGPR
-  // pair) plus a 32-bit lane offset, each with a constant byte offset.
-  // Issued through asm so that the compiler, which cannot tell the stages
-  // apart, does not make later LDS reads wait for every DMA; the tile
-  // pipeline waits on vmcnt itself.  One wait state separates the M0 write
-  // from the DMA.  The stage it writes is not read before the next barrier.
-  // The uniform operands pass through readfirstlane so that they are SGPRs
-  // even where the compiler cannot prove them uniform.
-  template <int kOff>
-  __device__ __forceinline__ static void dma16(const char* src, uint32_t lds_addr) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2"
+  // m0 + offset + 16 * lane, with m0 = lds_base + kM0 (lds_base uniform, in
+  // an SGPR since the tile's set-up): lane row address (64-bit VGPR pair,
+  // `off` form) or a uniform base (SGPR pair) plus a 32-bit lane offset,
+  // each with a constant byte offset.  Issued through asm so that the
+  // compiler, which cannot tell the stages apart, does not make later LDS
+  // reads wait for every DMA; the tile pipeline waits on vmcnt itself.  One
+  // wait state separates the M0 write from the DMA.  The stage it writes is
+  // not read before the next barrier.  Nothing here should wait on a VALU
+  // result (the readfirstlane is a copy once lds_base is in an SGPR): such a
+  // chain in front of each DMA stalls the in-order wave.
+  template <int kOff, int kM0>
+  __device__ __forceinline__ static void dma16(const char* src, uint32_t lds_base) {
+    asm volatile("s_add_u32 m0, %1, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%3"
                  :
-                 : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "i"(kOff)
-                 : "m0");
+                 : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base)), "i"(kM0), "i"(kOff)
+                 : "m0", "scc");
   }
-  template <int kOff>
-  __device__ __forceinline__ static void dma16s(uint32_t voff, const char* sbase,
-                                                uint32_t lds_addr) {
-    const uint64_t b = reinterpret_cast<uint64_t>(sbase);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
-    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32));
-    const uint64_t sb = (static_cast<uint64_t>(hi) << 32) | lo;
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3"
+  template <int kOff, int kM0>
+  __device__ __forceinline__ static void dma16s(uint32_t voff, const char* sbase, uint32_t lds_base) {
+    asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%4"
                  :
-                 : "v"(voff), "s"(sb), "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "i"(kOff)
-                 : "m0");
+                 : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base)), "i"(kM0),
+                   "i"(kOff)
+                 : "m0", "scc");
   }
 
   // One tile's DMAs for this wave.  DMA instruction I = wave + j NW covers
@@ -300,8 +297,12 @@ struct Attn {
   __device__ __forceinline__ TileDma prep_tile(int t, int pg, int inp) const {
     const int base = kv_begin + t * kTileKeys;
     TileDma d;
-    d.dst = lds_base + (t % kStages) * kCkvBytes + wave * 1024;
-    d.dst2 = lds_base + kKpeOff + (t % kKpeSlots) * kKpeBytes + wave * 1024 - kCkvBytes;
+    // (uniform: pinned to SGPRs here, or the compiler sinks a readfirstlane
+    // in front of every DMA)
+    d.dst = __builtin_amdgcn_readfirstlane(lds_base + (t % kStages) * kCkvBytes + wave * 1024);
+    d.dst2 = __builtin_amdgcn_readfirstlane(lds_base + kKpeOff + (t % kKpeSlots) * kKpeBytes +
+                                            wave * 1024 - kCkvBytes);
+    asm volatile("" : "+s"(d.dst), "+s"(d.dst2));
     if (kTileInPage) {
       const int rem = kv_end - 1 - base;  // keys past the item's end re-read its last key
       const int lane_c = ld_off + wave * 32;
@@ -333,12 +334,13 @@ struct Attn {
     constexpr int kOff = j * NW * 32;
     // The instruction offset moves the LDS destination as well as the
     // global address, so M0 takes it back off.
-    const uint32_t dst = (j * NW < kCkvDmas ? d.dst : d.dst2) + j * NW * 1024 - kOff;
+    constexpr int kM0 = j * NW * 1024 - kOff;
+    const uint32_t dbase = j * NW < kCkvDmas ? d.dst : d.dst2;
     const bool odd = NW == 1 ? (j & 1) : (wave & 1);
     if (kTileInPage)
-      dma16s<kOff>(odd ? d.voff_o : d.voff_e, d.sbase, dst);
+      dma16s<kOff, kM0>(odd ? d.voff_o : d.voff_e, d.sbase, dbase);
     else
-      dma16<kOff>(odd ? d.src_o : d.src_e, dst);
+      dma16<kOff, kM0>(odd ? d.src_o : d.src_e, dbase);
   }
 
   template <int j0, int j1>
@@ -473,7 +475,7 @@ struct Attn {
           const int base = kv_begin + t * kTileKeys;
           float x[16];
           {
-            TileDma d;
+            TileDma d{};  // (defined on every path: a phi with undef would put it in VGPRs)
             auto prep = [&] {
               d = prep_tile(t + kTilesAhead, kTileInPage ? __builtin_amdgcn_readfirstlane(pg_next) : 0,
                             cur_inp);

@@ -1,9 +1,9 @@
 // LSE merges for gfx950.
 //
 // Both kernels combine attention results over disjoint key segments through
-// their natural-log LSEs, the use the m-star page
-// "mstar.engine.resources.attn.flashinfer_mla" gives for the returned LSE
-// (FlashInferMLAManager.run: "for merging with another key segment"):
+// their natural-log LSEs, which is what the m-star page
+// "mstar.engine.resources.attn.flashinfer_mla" returns the LSE for
+// (FlashInferMLAManager.run):
 //   M = max_k s_k,  w_k = exp(s_k - M),  v = sum w_k v_k / sum w_k,
 //   s = M + ln sum w_k,  and (0, -inf) when every segment is empty.
 // Both are bandwidth-bound elementwise passes over [tokens, heads, 512].
@@ -27,39 +27,60 @@ __device__ __forceinline__ float bf16_hi(unsigned w) {
 // Split-KV partials -> final bf16 output + LSE.  A piece k holds its
 // normalised output o_k (bf16) and its LSE s_k.  One block of 128 threads
 // per (merge entry, head); each thread owns 4 consecutive latent columns.
-__global__ __launch_bounds__(128) void split_merge_kernel(SplitMergeArgs a) {
-  const int h = blockIdx.x;
-  const MergeItem m = a.merges[blockIdx.y];
+// One wave per (merge item, head): lane l owns columns 8l .. 8l+7.  The
+// slots' LSEs are read lane-parallel for their maximum; then the partial
+// rows go out in batches of kBatch independent loads (with the slot LSEs as
+// uniform loads), so a token split in n pieces waits about n / kBatch load
+// latencies instead of n.
+__global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeArgs a) {
+  constexpr int kBatch = 8;
+  const int lane = threadIdx.x & 63;
   const int H = a.num_heads;
-  const int c = threadIdx.x * 4;
+  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pair >= a.num_merges * H) return;
+  const int mi = pair / H, h = pair - mi * H;
+  const MergeItem m = a.merges[mi];
+  const int n = m.num_slots;
+  const int64_t base = static_cast<int64_t>(m.first_slot) * H + h;  // slot k: base + k H
   float M = -INFINITY;
-  for (int k = 0; k < m.num_slots; ++k)
-    M = fmaxf(M, a.part_lse[static_cast<int64_t>(m.first_slot + k) * H + h]);
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k = lane; k < n; k += 64) M = fmaxf(M, a.part_lse[base + static_cast<int64_t>(k) * H]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
   if (M != -INFINITY) {
-    for (int k = 0; k < m.num_slots; ++k) {
-      const int64_t sh = static_cast<int64_t>(m.first_slot + k) * H + h;
-      const float s = a.part_lse[sh];
-      const float w = (s == -INFINITY) ? 0.f : expf(s - M);
-      const u32x2_t r = *reinterpret_cast<const u32x2_t*>(a.part_o + sh * kLoraRank + c);
-      const f32x4_t v = {bf16_lo(r[0]), bf16_hi(r[0]), bf16_lo(r[1]), bf16_hi(r[1])};
-      acc += w * v;
-      wsum += w;
+    for (int k0 = 0; k0 < n; k0 += kBatch) {
+      u32x4_t r[kBatch];
+      float s[kBatch];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int k = k0 + b < n ? k0 + b : n - 1;  // (a repeated slot gets weight 0)
+        const int64_t sh = base + static_cast<int64_t>(k) * H;
+        s[b] = a.part_lse[sh];
+        r[b] = *reinterpret_cast<const u32x4_t*>(a.part_o + sh * kLoraRank + lane * 8);
+      }
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const float w = (k0 + b >= n || s[b] == -INFINITY) ? 0.f : expf(s[b] - M);
+        wsum += w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[2 * j] += w * bf16_lo(r[b][j]);
+          acc[2 * j + 1] += w * bf16_hi(r[b][j]);
+        }
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   const int64_t th = static_cast<int64_t>(m.token) * H + h;
-  u32x2_t o;
-  o[0] = to_bf16(acc[0] * inv) | (static_cast<unsigned>(to_bf16(acc[1] * inv)) << 16);
-  o[1] = to_bf16(acc[2] * inv) | (static_cast<unsigned>(to_bf16(acc[3] * inv)) << 16);
-  *reinterpret_cast<u32x2_t*>(a.out + th * kLoraRank + c) = o;
-  if (a.lse && threadIdx.x == 0) a.lse[th] = wsum > 0.f ? M + logf(wsum) : -INFINITY;
+  u32x4_t o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    o[j] = to_bf16(acc[2 * j] * inv) | (static_cast<unsigned>(to_bf16(acc[2 * j + 1] * inv)) << 16);
+  *reinterpret_cast<u32x4_t*>(a.out + th * kLoraRank + lane * 8) = o;
+  if (a.lse && lane == 0) a.lse[th] = wsum > 0.f ? M + logf(wsum) : -INFINITY;
 }
 
-// Two-segment merge.  One wave per (token, head): lane i owns columns
-// 8i .. 8i+7 (16 bytes of each bf16 input).  All lanes read s_a / s_b in the
-// same instruction before any lane writes s_out, so s_out may alias s_a.
 __global__ __launch_bounds__(256) void merge_state_kernel(const uint16_t* v_a,
                                                           const float* s_a,
                                                           const uint16_t* v_b,
@@ -96,8 +117,9 @@ __global__ __launch_bounds__(256) void merge_state_kernel(const uint16_t* v_a,
 
 hipError_t launch_split_merge(const SplitMergeArgs& a, hipStream_t stream) {
   if (a.num_merges <= 0) return hipSuccess;
-  hipLaunchKernelGGL(split_merge_kernel, dim3(a.num_heads, a.num_merges), dim3(128), 0, stream,
-                     a);
+  const int64_t pairs = static_cast<int64_t>(a.num_merges) * a.num_heads;
+  hipLaunchKernelGGL(split_merge_kernel, dim3(static_cast<unsigned>((pairs + 3) / 4)), dim3(256), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
