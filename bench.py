@@ -103,16 +103,23 @@ def run_steps(w, steps, warmup, copies=3):
     qo, kvp, idx, last = (np.ascontiguousarray(a, dtype=np.int32) for a in
                           (w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_len))
 
-    def step(k, ev=None):
+    def do_plan():
         plan.plan(qo, kvp, idx, last, causal=w.causal, sm_scale=w.sm_scale,
                   num_cache_pages=w.num_pages)
+
+    # A step is one plan and one run.  As in a serving loop, the plan of the
+    # next step is made while this step's kernels run (its upload overlaps
+    # them); the run events time the kernels.
+    def step(k, ev=None):
         c = k % copies
         if ev is not None:
             ev[0].record()
         plan.run(qns[c], qps[c], kvs[c], out=outs[c], lse=lses[c])
         if ev is not None:
             ev[1].record()
+        do_plan()
 
+    do_plan()
     for k in range(warmup):
         step(k)
     torch.cuda.synchronize()

@@ -42,34 +42,50 @@ struct CostModel {
 
 constexpr int kMinPieceTiles = 2;
 
-// Greedy contiguous fill of `budget` cost per worker.  Returns the number of
-// workers used (may exceed num_workers only if forced onto the last one,
-// which is signalled through *overflow).
+// Greedy contiguous fill of `budget` cost per worker; *max_load receives
+// the largest worker cost (above the budget only where the last worker had
+// to take the rest).  kEmit = false only computes that cost (the budget
+// search calls it many times per plan); kEmit = true also records the items.
+// Items come out in worker order: those of worker k are
+// (*items)[(*first)[k] .. (*first)[k + 1]).
+template <bool kEmit>
 void fill(const std::vector<TokenWork>& toks, const CostModel& cm, double budget,
-          int32_t num_workers, std::vector<std::vector<WorkItem>>* per_worker,
+          int32_t num_workers, std::vector<WorkItem>* items, std::vector<int32_t>* first,
           double* max_load) {
-  per_worker->assign(num_workers, {});
-  std::vector<double> load(num_workers, 0.0);
+  if (kEmit) {
+    items->clear();
+    first->assign(num_workers + 1, 0);
+  }
   int k = 0;
+  double cur = 0.0;  // cost on worker k
+  double peak = 0.0;  // largest cost of the workers before k
+  auto next_worker = [&] {
+    peak = std::max(peak, cur);
+    cur = 0.0;
+    ++k;
+    if (kEmit) (*first)[k] = static_cast<int32_t>(items->size());
+  };
+  auto emit = [&](const WorkItem& w) {
+    if (kEmit) items->push_back(w);
+  };
   for (const TokenWork& tw : toks) {
     if (tw.tiles == 0) {
-      (*per_worker)[k].push_back(WorkItem{tw.token, tw.row, 0, 0, -1, {0, 0, 0}});
-      load[k] += cm.item;
-      if (load[k] >= budget && k < num_workers - 1) ++k;
+      emit(WorkItem{tw.token, tw.row, 0, 0, -1, {0, 0, 0}});
+      cur += cm.item;
+      if (cur >= budget && k < num_workers - 1) next_worker();
       continue;
     }
     int a = 0;
     bool split = false;
     while (a < tw.tiles) {
       const int rem = tw.tiles - a;
-      const double free = budget - load[k];
+      const double free = budget - cur;
       const bool last = k == num_workers - 1;
       // The whole remainder as one item, if it is not too long and fits.
       if (rem <= kMaxItemTiles &&
           (rem + cm.item + (split ? cm.split : 0.0) <= free + kMinPieceTiles || last)) {
-        const int32_t kb = a * kTileKeys;
-        (*per_worker)[k].push_back(WorkItem{tw.token, tw.row, kb, tw.visible, split ? 0 : -1, {0, 0, 0}});
-        load[k] += rem + cm.item + (split ? cm.split : 0.0);
+        emit(WorkItem{tw.token, tw.row, a * kTileKeys, tw.visible, split ? 0 : -1, {0, 0, 0}});
+        cur += rem + cm.item + (split ? cm.split : 0.0);
         a = tw.tiles;
         break;
       }
@@ -78,21 +94,20 @@ void fill(const std::vector<TokenWork>& toks, const CostModel& cm, double budget
       int cap = rem > kMaxItemTiles ? kMaxItemTiles : rem - kMinPieceTiles;
       int take = last ? cap : std::min(cap, static_cast<int>(free - cm.item - cm.split));
       if (take >= kMinPieceTiles) {
-        const int32_t kb = a * kTileKeys;
-        (*per_worker)[k].push_back(
-            WorkItem{tw.token, tw.row, kb, (a + take) * kTileKeys, 0, {0, 0, 0}});
-        load[k] += take + cm.item + cm.split;
+        emit(WorkItem{tw.token, tw.row, a * kTileKeys, (a + take) * kTileKeys, 0, {0, 0, 0}});
+        cur += take + cm.item + cm.split;
         a += take;
         split = true;
-        if (!last && load[k] >= budget - kMinPieceTiles) ++k;  // this worker is full
+        if (!last && cur >= budget - kMinPieceTiles) next_worker();  // this worker is full
         continue;
       }
-      ++k;  // no room left on this worker (never the last one here)
+      next_worker();  // no room left on this worker (never the last one here)
     }
-    if (load[k] >= budget && k < num_workers - 1) ++k;
+    if (cur >= budget && k < num_workers - 1) next_worker();
   }
-  *max_load = 0.0;
-  for (double l : load) *max_load = std::max(*max_load, l);
+  *max_load = std::max(peak, cur);
+  if (kEmit)
+    for (int j = k + 1; j <= num_workers; ++j) (*first)[j] = static_cast<int32_t>(items->size());
 }
 
 }  // namespace
@@ -173,12 +188,13 @@ mla_status build_schedule(const PlanArgs& a, Schedule* out) {
   const int32_t W = a.num_workers;
   // Smallest per-worker budget whose greedy fill fits on W workers (split
   // costs are only known after a fill, so search for it).
-  std::vector<std::vector<WorkItem>> per_worker;
+  std::vector<WorkItem> items;
+  std::vector<int32_t> first;
   double max_load = 0.0;
   double lo = std::max(total / W, 4.0 + cm.item);
   double hi = lo;
   auto fits = [&](double budget) {
-    fill(toks, cm, budget, W, &per_worker, &max_load);
+    fill<false>(toks, cm, budget, W, nullptr, nullptr, &max_load);
     return max_load <= budget + kMinPieceTiles;
   };
   while (!fits(hi)) hi *= 1.25;
@@ -186,12 +202,12 @@ mla_status build_schedule(const PlanArgs& a, Schedule* out) {
     const double mid = 0.5 * (lo + hi);
     if (fits(mid)) hi = mid; else lo = mid;
   }
-  fill(toks, cm, hi, W, &per_worker, &max_load);
+  items.reserve(toks.size() + 2 * static_cast<size_t>(W));
+  fill<true>(toks, cm, hi, W, &items, &first, &max_load);
 
   // Partial slots: tokens that ended up in more than one item.
   std::vector<int32_t> pieces(static_cast<size_t>(T), 0);
-  for (auto& lst : per_worker)
-    for (WorkItem& it : lst) ++pieces[it.token];
+  for (const WorkItem& it : items) ++pieces[it.token];
   std::vector<int32_t> first_slot(static_cast<size_t>(T), -1);
   std::vector<int32_t> next_slot(static_cast<size_t>(T), 0);
   Schedule s;
@@ -203,14 +219,13 @@ mla_status build_schedule(const PlanArgs& a, Schedule* out) {
       slots += pieces[t];
     }
   }
-  for (auto& lst : per_worker)
-    for (WorkItem& it : lst) {
-      if (pieces[it.token] > 1) {
-        it.slot = first_slot[it.token] + next_slot[it.token]++;
-      } else {
-        it.slot = -1;
-      }
+  for (WorkItem& it : items) {
+    if (pieces[it.token] > 1) {
+      it.slot = first_slot[it.token] + next_slot[it.token]++;
+    } else {
+      it.slot = -1;
     }
+  }
 
   // Launch order: workgroups are dispatched round-robin over the 8 XCDs of
   // the device (each with its own L2), so consecutive logical workers (which
@@ -226,9 +241,9 @@ mla_status build_schedule(const PlanArgs& a, Schedule* out) {
   }
   s.worker_indptr.assign(W + 1, 0);
   for (int p = 0; p < W; ++p) {
-    const auto& lst = per_worker[logical_of[p]];
-    s.worker_indptr[p + 1] = s.worker_indptr[p] + static_cast<int32_t>(lst.size());
-    s.items.insert(s.items.end(), lst.begin(), lst.end());
+    const int l = logical_of[p];
+    s.worker_indptr[p + 1] = s.worker_indptr[p] + (first[l + 1] - first[l]);
+    s.items.insert(s.items.end(), items.begin() + first[l], items.begin() + first[l + 1]);
   }
   s.num_workers = W;
   s.batch = B;
