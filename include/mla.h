@@ -94,12 +94,15 @@ mla_status mla_plan_create(mla_plan_t* out, int32_t device, int32_t num_heads,
  * kept.  kv_indices must hold at least kv_indptr[batch] entries.  Page ids
  * must lie in [0, num_cache_pages).
  *
- * The host-to-device copy is asynchronous on `stream`.  Before it overwrites
- * its pinned staging buffer, mla_plan waits for the previous plan's copy to
- * finish, so planning step N+1 never races step N's in-flight copy.  The
- * first plan, and any plan that outgrows the device buffers, synchronises
- * `stream` while it (re)allocates; later plans of equal or smaller size
- * allocate nothing.  mla_run must be called on the same stream (or one
+ * The schedule is staged in one of two pinned host slots, alternating
+ * between plans.  A small schedule (at most two work items per compute
+ * unit, as in decode) is read by the kernels straight from that slot; a
+ * larger one is copied asynchronously on `stream` to the plan's device
+ * buffer.  Before refilling a slot, mla_plan waits for the last copy from it
+ * and the last mla_run that read it, so planning step N+1 never races step
+ * N.  The first plan, and any plan that outgrows the buffers, synchronises
+ * the device while it (re)allocates; later plans of equal or smaller size
+ * allocate nothing.  mla_run must be called on `stream` (or a stream
  * ordered after it).
  *
  * Errors: MLA_E_INVALID for a malformed table (indptr[0] != 0, decreasing
@@ -113,9 +116,10 @@ mla_status mla_plan(mla_plan_t plan, const int32_t* qo_indptr, const int32_t* kv
 
 /* Run the planned batch (FlashInferMLAWrapper.run): all pointers are device
  * memory with the layouts above; `lse` may be NULL when not wanted.  The call
- * only enqueues kernels on `stream` (no allocation, no synchronisation), so
- * it may be captured in a HIP graph.  The plan must not be re-planned while a
- * captured graph that reads it may still replay.
+ * only enqueues kernels on `stream`, and an event that later plans wait on
+ * (no allocation, no synchronisation), so it may be captured in a HIP graph;
+ * the event is left out under capture.  The plan must not be re-planned while
+ * a captured graph that reads it may still replay.
  *
  * Errors: MLA_E_STATE without a successful mla_plan; MLA_E_INVALID for a NULL
  * required pointer; MLA_E_HIP if a launch fails. */

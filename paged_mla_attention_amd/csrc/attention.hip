@@ -371,11 +371,10 @@ struct Attn {
     for (int it = w_begin; it < w_end; ++it) {
       const_i32_t* item = (const_i32_t*)(a.items) + it * 8;  // WorkItem fields
       token = item[0];
-      const int row = item[1];
       kv_begin = item[2];
       kv_end = item[3];
       slot = item[4];
-      page_base = ((const_i32_t*)(a.kv_indptr))[row];
+      page_base = item[5];  // kv_indptr[row]
       const int ntiles = (kv_end - kv_begin + kTileKeys - 1) / kTileKeys;
 
       f32x16_t o[NW][kDimBlocks];

@@ -1,12 +1,17 @@
 // C ABI of the library (include/mla.h): plan objects, the host-to-device
 // schedule copy with its staging fence, and the kernel launches.
 //
-// The staging fence follows the hazard the m-star page
+// The staging fences follow the hazard the m-star page
 // "mstar.engine.resources.attn.flashinfer_mla" describes under
 // FlashInferMLAManager.force_double_buffer: a plan that stages into a reused
-// host buffer and copies it to the device without blocking must not
-// overwrite that buffer before the previous copy has been consumed.  Here
-// every plan waits on the event recorded after its previous copy.
+// host buffer without blocking must not overwrite that buffer before its
+// previous contents have been consumed.  Plans alternate between two pinned
+// host slots.  A small schedule (at most two items per worker, as in
+// decode) is read by the kernels straight from its pinned slot, which saves
+// the upload that would otherwise sit between two steps' kernels; a larger
+// one is copied to the device buffer on the plan's stream.  Before
+// refilling a slot, a plan waits for the last copy from it and the last run
+// that read it.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -60,10 +65,17 @@ struct mla_plan_s {
   float scale_log2 = 0.f;
   mla::Schedule sched;
 
-  // Pinned host staging and its device mirror: worker_indptr | items |
-  // merges | kv_indptr | kv_indices, each section 256-byte aligned.
-  char* h_stage = nullptr;
-  size_t h_stage_cap = 0;
+  // Pinned host staging slots and the device mirror: worker_indptr | items
+  // | merges | kv_indptr | kv_indices, each section 256-byte aligned.
+  struct HostSlot {
+    char* h_stage = nullptr;
+    size_t cap = 0;
+    hipEvent_t done = nullptr;  // after the last copy from / run reading the slot
+    bool pending = false;
+  };
+  HostSlot slot[2];
+  int cur = 0;              // slot of the current plan
+  bool direct = false;      // the kernels read the schedule from the host slot
   char* d_stage = nullptr;
   size_t d_stage_cap = 0;
   size_t off_items = 0, off_merges = 0, off_kv_indptr = 0, off_kv_indices = 0;
@@ -73,9 +85,22 @@ struct mla_plan_s {
   float* d_part = nullptr;
   size_t part_cap = 0;  // floats
 
-  hipEvent_t h2d_done = nullptr;
-  bool h2d_pending = false;
 };
+
+namespace {
+
+void release(mla_plan_s* p) {
+  for (auto& sl : p->slot) {
+    if (sl.pending) (void)hipEventSynchronize(sl.done);
+    if (sl.done) (void)hipEventDestroy(sl.done);
+    if (sl.h_stage) (void)hipHostFree(sl.h_stage);
+  }
+  if (p->d_stage) (void)hipFree(p->d_stage);
+  if (p->d_part) (void)hipFree(p->d_part);
+  delete p;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -104,10 +129,12 @@ mla_status mla_plan_create(mla_plan_t* out, int32_t device, int32_t num_heads,
   p->num_heads = num_heads;
   p->page_size = page_size;
   p->num_workers = cus > 0 ? cus : 1;
-  e = hipEventCreateWithFlags(&p->h2d_done, hipEventDisableTiming);
-  if (e != hipSuccess) {
-    delete p;
-    return hip_fail(e, "hipEventCreate");
+  for (auto& sl : p->slot) {
+    e = hipEventCreateWithFlags(&sl.done, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      release(p);
+      return hip_fail(e, "hipEventCreate");
+    }
   }
   *out = p;
   return MLA_OK;
@@ -150,29 +177,33 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
   const size_t off_idx = off_kvp + align_up(n_kvp);
   const size_t total = off_idx + align_up(n_idx_pad);
 
-  // The previous copy must have read the staging buffer before we refill it.
+  // This plan's host slot: the last copy from it and the last run that read
+  // it must be done before it is refilled.
   hipError_t e;
-  if (p->h2d_pending) {
-    e = hipEventSynchronize(p->h2d_done);
+  const int si = p->cur ^ 1;
+  auto& sl = p->slot[si];
+  if (sl.pending) {
+    e = hipEventSynchronize(sl.done);
     if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
-    p->h2d_pending = false;
+    sl.pending = false;
   }
-  if (total > p->h_stage_cap) {
-    if (p->h_stage) (void)hipHostFree(p->h_stage);
-    p->h_stage = nullptr;
-    p->h_stage_cap = 0;
-    e = hipHostMalloc(reinterpret_cast<void**>(&p->h_stage), total, hipHostMallocDefault);
+  if (total > sl.cap) {
+    if (sl.h_stage) (void)hipHostFree(sl.h_stage);
+    sl.h_stage = nullptr;
+    sl.cap = 0;
+    e = hipHostMalloc(reinterpret_cast<void**>(&sl.h_stage), total, hipHostMallocDefault);
     if (e != hipSuccess) return hip_fail(e, "hipHostMalloc");
-    p->h_stage_cap = total;
+    sl.cap = total;
   }
+  const bool direct = s.items.size() <= 2 * static_cast<size_t>(p->num_workers);
   // Partials: bf16 output rows [slots, H, 512] then fp32 LSE [slots, H].
   const size_t part_floats =
       static_cast<size_t>(s.num_slots) * p->num_heads * (mla::kLoraRank / 2 + 1);
-  if (total > p->d_stage_cap || part_floats > p->part_cap) {
+  if ((!direct && total > p->d_stage_cap) || part_floats > p->part_cap) {
     // Buffers may still be read by enqueued kernels of an earlier plan.
     e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-    if (total > p->d_stage_cap) {
+    if (!direct && total > p->d_stage_cap) {
       if (p->d_stage) (void)hipFree(p->d_stage);
       p->d_stage = nullptr;
       p->d_stage_cap = 0;
@@ -189,17 +220,24 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
       p->part_cap = part_floats;
     }
   }
-  std::memcpy(p->h_stage, s.worker_indptr.data(), n_wi);
-  if (n_items) std::memcpy(p->h_stage + off_items, s.items.data(), n_items);
-  if (n_merges) std::memcpy(p->h_stage + off_merges, s.merges.data(), n_merges);
-  if (s.batch > 0) std::memcpy(p->h_stage + off_kvp, kv_indptr, n_kvp);
-  if (n_idx) std::memcpy(p->h_stage + off_idx, kv_indices, n_idx);
-  std::memset(p->h_stage + off_idx + n_idx, 0, n_idx_pad - n_idx);
-  e = hipMemcpyAsync(p->d_stage, p->h_stage, total, hipMemcpyHostToDevice, stream);
-  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
-  e = hipEventRecord(p->h2d_done, stream);
-  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-  p->h2d_pending = true;
+  char* h = sl.h_stage;
+  std::memcpy(h, s.worker_indptr.data(), n_wi);
+  if (n_items) std::memcpy(h + off_items, s.items.data(), n_items);
+  if (n_merges) std::memcpy(h + off_merges, s.merges.data(), n_merges);
+  if (s.batch > 0) std::memcpy(h + off_kvp, kv_indptr, n_kvp);
+  if (n_idx) std::memcpy(h + off_idx, kv_indices, n_idx);
+  std::memset(h + off_idx + n_idx, 0, n_idx_pad - n_idx);
+  if (!direct) {
+    // (Stream order keeps the copy behind the runs that read the device
+    // buffer before.)
+    e = hipMemcpyAsync(p->d_stage, h, total, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+    e = hipEventRecord(sl.done, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    sl.pending = true;
+  }
+  p->cur = si;
+  p->direct = direct;
 
   p->off_items = off_items;
   p->off_merges = off_merges;
@@ -233,10 +271,12 @@ mla_status mla_run(mla_plan_t p, const void* q_nope, const void* q_pe, const voi
   a.lse = lse;
   a.part_o = reinterpret_cast<uint16_t*>(p->d_part);
   a.part_lse = p->d_part ? p->d_part + slots_h * (mla::kLoraRank / 2) : nullptr;
-  a.worker_indptr = reinterpret_cast<const int32_t*>(p->d_stage);
-  a.items = reinterpret_cast<const mla::WorkItem*>(p->d_stage + p->off_items);
-  a.kv_indptr = reinterpret_cast<const int32_t*>(p->d_stage + p->off_kv_indptr);
-  a.kv_indices = reinterpret_cast<const int32_t*>(p->d_stage + p->off_kv_indices);
+  auto& sl = p->slot[p->cur];
+  const char* d = p->direct ? sl.h_stage : p->d_stage;
+  a.worker_indptr = reinterpret_cast<const int32_t*>(d);
+  a.items = reinterpret_cast<const mla::WorkItem*>(d + p->off_items);
+  a.kv_indptr = reinterpret_cast<const int32_t*>(d + p->off_kv_indptr);
+  a.kv_indices = reinterpret_cast<const int32_t*>(d + p->off_kv_indices);
   a.num_heads = p->num_heads;
   a.page_size = p->page_size;
   a.scale_log2 = p->scale_log2;
@@ -246,13 +286,26 @@ mla_status mla_run(mla_plan_t p, const void* q_nope, const void* q_pe, const voi
     mla::SplitMergeArgs m{};
     m.part_o = a.part_o;
     m.part_lse = a.part_lse;
-    m.merges = reinterpret_cast<const mla::MergeItem*>(p->d_stage + p->off_merges);
+    m.merges = reinterpret_cast<const mla::MergeItem*>(d + p->off_merges);
     m.out = a.out;
     m.lse = lse;
     m.num_heads = p->num_heads;
     m.num_merges = static_cast<int32_t>(s.merges.size());
     e = mla::launch_split_merge(m, stream);
     if (e != hipSuccess) return hip_fail(e, "split-merge launch");
+  }
+  if (p->direct) {
+    // The host slot is read by these kernels.  (Under stream capture a
+    // replay reads it whenever it runs: the caller must not re-plan twice
+    // while such a graph may still replay.)
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &cap);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+    if (cap == hipStreamCaptureStatusNone) {
+      e = hipEventRecord(sl.done, stream);
+      if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+      sl.pending = true;
+    }
   }
   return MLA_OK;
 }
@@ -276,12 +329,7 @@ mla_status mla_merge_state(const void* v_a, const float* s_a, const void* v_b, c
 void mla_plan_destroy(mla_plan_t p) {
   if (!p) return;
   DeviceGuard g(p->device);
-  if (p->h2d_pending) (void)hipEventSynchronize(p->h2d_done);
-  if (p->h2d_done) (void)hipEventDestroy(p->h2d_done);
-  if (p->h_stage) (void)hipHostFree(p->h_stage);
-  if (p->d_stage) (void)hipFree(p->d_stage);
-  if (p->d_part) (void)hipFree(p->d_part);
-  delete p;
+  release(p);
 }
 
 mla_status mla_plan_stats(mla_plan_t p, int32_t* num_workers, int64_t* num_items,

@@ -70,7 +70,7 @@ void fill(const std::vector<TokenWork>& toks, const CostModel& cm, double budget
   };
   for (const TokenWork& tw : toks) {
     if (tw.tiles == 0) {
-      emit(WorkItem{tw.token, tw.row, 0, 0, -1, {0, 0, 0}});
+      emit(WorkItem{tw.token, tw.row, 0, 0, -1, 0, {0, 0}});
       cur += cm.item;
       if (cur >= budget && k < num_workers - 1) next_worker();
       continue;
@@ -84,7 +84,7 @@ void fill(const std::vector<TokenWork>& toks, const CostModel& cm, double budget
       // The whole remainder as one item, if it is not too long and fits.
       if (rem <= kMaxItemTiles &&
           (rem + cm.item + (split ? cm.split : 0.0) <= free + kMinPieceTiles || last)) {
-        emit(WorkItem{tw.token, tw.row, a * kTileKeys, tw.visible, split ? 0 : -1, {0, 0, 0}});
+        emit(WorkItem{tw.token, tw.row, a * kTileKeys, tw.visible, split ? 0 : -1, 0, {0, 0}});
         cur += rem + cm.item + (split ? cm.split : 0.0);
         a = tw.tiles;
         break;
@@ -94,7 +94,7 @@ void fill(const std::vector<TokenWork>& toks, const CostModel& cm, double budget
       int cap = rem > kMaxItemTiles ? kMaxItemTiles : rem - kMinPieceTiles;
       int take = last ? cap : std::min(cap, static_cast<int>(free - cm.item - cm.split));
       if (take >= kMinPieceTiles) {
-        emit(WorkItem{tw.token, tw.row, a * kTileKeys, (a + take) * kTileKeys, 0, {0, 0, 0}});
+        emit(WorkItem{tw.token, tw.row, a * kTileKeys, (a + take) * kTileKeys, 0, 0, {0, 0}});
         cur += take + cm.item + cm.split;
         a += take;
         split = true;
@@ -220,6 +220,7 @@ mla_status build_schedule(const PlanArgs& a, Schedule* out) {
     }
   }
   for (WorkItem& it : items) {
+    it.page_base = a.kv_indptr[it.row];
     if (pieces[it.token] > 1) {
       it.slot = first_slot[it.token] + next_slot[it.token]++;
     } else {

@@ -30,7 +30,8 @@ struct WorkItem {
   int32_t kv_begin;  // first key (multiple of kTileKeys)
   int32_t kv_end;    // one past the last key
   int32_t slot;      // -1: final output; >= 0: partial slot
-  int32_t pad[3];
+  int32_t page_base; // kv_indptr[row]: the row's first entry in kv_indices
+  int32_t pad[2];
 };
 static_assert(sizeof(WorkItem) == 32, "work item is 8 int32");
 

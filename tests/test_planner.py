@@ -48,6 +48,7 @@ def _check_invariants(w, s, workers):
     for it in items:
         t, row, kb, ke, slot = (int(x) for x in it[:5])
         assert 0 <= t < T and row == row_of[t]
+        assert int(it[5]) == int(w.kv_indptr[row])  # the row's page-list base
         assert kb % TILE == 0 and 0 <= kb <= ke <= vis[t]
         covered[t].append((kb, ke, slot))
     slot_seen = set()
