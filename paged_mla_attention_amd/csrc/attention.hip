@@ -583,8 +583,7 @@ struct Attn {
     for (int i = 0; i < kAhead; ++i) kbuf[i] = kload(i);
     static_for<kQSteps>([&](auto kc) {
       constexpr int ks = decltype(kc)::value;
-      bf16x8_t k0 = kbuf[ks % kAhead];
-      in_vgpr(k0);  // (at the use: the asm waits for the load)
+      const bf16x8_t k0 = kbuf[ks % kAhead];  // (the asm operand is a VGPR)
       if constexpr (ks + kAhead < kQSteps) kbuf[ks % kAhead] = kload(ks + kAhead);
       if constexpr (ks == 0)
         mfma_v_first(acc, k0, q[ks]);
