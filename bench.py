@@ -2,8 +2,8 @@
 """Benchmark: paged MLA decode on one MI355X.
 
 One step = one pass of the whole path over one batch: ``mla_plan`` (host
-planning + asynchronous copy of the schedule) followed by ``mla_run``
-(attention kernel + split-KV merge kernel).  The workload is the decode batch
+planning, schedule staged for the device) and ``mla_run`` (attention kernel
++ split-KV merge kernel); the plan of step k+1 is made while run k executes.  The workload is the decode batch
 of 64 rows, 128 heads, page_size 64, kv lengths uniform in [512, 4096]
 (seed 1002), with inputs resident in HBM.  Three independent copies of the KV
 cache, queries and outputs are rotated so the 256 MB last-level cache cannot
@@ -12,7 +12,9 @@ serve a step from the previous one.
 ``value`` is decode throughput in GB/s of algorithmic bytes (latent rows read
 once, queries read, outputs and LSE written, index arrays) per wall-clock
 step.  The JSON line also carries the chunked-prefill throughput (TFLOP/s),
-the kernel roofline and the fp64 CPU oracle's throughput on this host.
+the long-context decode and mixed ragged batch (with its extra segment and
+the ``mla_merge_state`` of the two results), each against its roofline, the
+kernel roofline and the fp64 CPU oracle's throughput on this host.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -136,6 +138,64 @@ def run_steps(w, steps, warmup, copies=3):
     return wall * 1e3, run_ms, stats
 
 
+def roofline_entry(w, run_ms, nbytes, flops):
+    """Throughput of one mla_run against the bound that applies to it."""
+    secs = run_ms * 1e-3
+    gbs, tfs = nbytes / secs / 1e9, flops / secs / 1e12
+    hbm_t, mfma_t = nbytes / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    bound = "hbm" if hbm_t >= mfma_t else "mfma"
+    return {"workload": w.name, "run_ms": round(run_ms, 4), "GB_s": round(gbs, 1),
+            "TFLOP_s": round(tfs, 1), "bound": bound,
+            "frac": round((gbs / HBM_PEAK_GBS) if bound == "hbm" else (tfs / MFMA_BF16_PEAK_TFLOPS), 4),
+            "algorithmic_bytes": nbytes, "algorithmic_flops": flops}
+
+
+def other_workloads(steps):
+    """The long-context decode and the mixed ragged batch (with its extra
+    segment and the LSE merge of the two results), timed the same way."""
+    import torch
+
+    import paged_mla_attention_amd as pm
+    out = {}
+    wl = W.long_decode()
+    b, f = algorithmic(wl)
+    _, run_ms, stats = run_steps(wl, steps, 3, copies=1)
+    out["long_decode"] = dict(roofline_entry(wl, run_ms, b, f), plan=stats)
+    print(f"[bench] long decode: mla_run {run_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+
+    wm = W.mixed()
+    b, f = algorithmic(wm)
+    _, run_ms, _ = run_steps(wm, max(3, steps // 5), 2, copies=1)
+    out["mixed"] = roofline_entry(wm, run_ms, b, f)
+    we = wm.extra
+    b, f = algorithmic(we)
+    _, run_ms, _ = run_steps(we, max(3, steps // 5), 2, copies=1)
+    out["mixed_extra_segment"] = roofline_entry(we, run_ms, b, f)
+    # mla_merge_state over the two results: bf16 [T, H, 512] x 3 + fp32 LSEs
+    T, H = wm.num_tokens, wm.num_heads
+    va = torch.randn(T, H, 512, device="cuda").to(torch.bfloat16)
+    vb = torch.randn(T, H, 512, device="cuda").to(torch.bfloat16)
+    sa, sb = torch.randn(T, H, device="cuda"), torch.randn(T, H, device="cuda")
+    vo, so = torch.empty_like(va), torch.empty_like(sa)
+    for _ in range(3):
+        pm.merge_state(va, sa, vb, sb, vo, so)
+    n = 20
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        pm.merge_state(va, sa, vb, sb, vo, so)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    mbytes = T * H * (3 * 1024 + 3 * 4)
+    out["merge_state"] = {"workload": f"mla_merge_state T={T} H={H}", "run_ms": round(ms, 4),
+                          "GB_s": round(mbytes / (ms * 1e-3) / 1e9, 1), "bound": "hbm",
+                          "frac": round(mbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "algorithmic_bytes": mbytes}
+    print("[bench] mixed batch, extra segment and merge done", file=sys.stderr, flush=True)
+    return out
+
+
 def cpu_baseline(w, target_s=10.0):
     """The fp64 oracle on this host's cores over whole repeats of the batch."""
     import oracle
@@ -228,6 +288,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the long-decode and mixed-batch workloads")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the chunked-prefill workload (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -284,6 +346,10 @@ def main():
                    "algorithmic_flops": pflops, "algorithmic_bytes": pbytes}
         print(f"[bench] prefill: {p_ms:.3f} ms/step", file=sys.stderr, flush=True)
 
+    others = None
+    if not args.no_prefill and not args.no_others:
+        others = other_workloads(max(10, args.steps // 2))
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w)
@@ -312,6 +378,7 @@ def main():
                      "duration_us": round(run_ms * 1e3, 2), "algorithmic_bytes": nbytes,
                      "algorithmic_flops": flops, "plan": stats},
         "prefill": prefill,
+        "other_workloads": others,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
