@@ -11,6 +11,7 @@ Run ``python -m paged_mla_attention_amd.build`` (or call :func:`build`).
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -40,8 +41,25 @@ def _run(cmd):
     return r.stdout
 
 
+def _stack_users(remarks: str):
+    """Kernels whose resource-usage remarks report scratch (private stack)
+    memory: a spill or a value the compiler could not keep in registers.
+    Either puts memory loads, and waits on them, inside the key loop."""
+    bad, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name and int(m.group(1)) > 0:
+            bad.append(f"{name} ({m.group(1)} bytes/lane)")
+    return bad
+
+
 def build_library(out: str = LIB, extra=()) -> str:
-    """Compile every HIP/C++ source into one shared library for gfx950."""
+    """Compile every HIP/C++ source into one shared library for gfx950.
+    Fails if any kernel uses scratch memory."""
     srcs = [os.path.join(CSRC, s) for s in HIP_SOURCES]
     tmp = out + ".tmp"
     cmd = [
@@ -49,9 +67,13 @@ def build_library(out: str = LIB, extra=()) -> str:
         # Keep the compiler from emitting packed fp32 VALU ops.
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-I", INCLUDE, "-Wall", "-Wno-unused-function",
+        "-Rpass-analysis=kernel-resource-usage",
         *extra, *srcs, "-o", tmp,
     ]
-    _run(cmd)
+    bad = _stack_users(_run(cmd))
+    if bad:
+        os.remove(tmp)
+        raise RuntimeError("kernels use scratch memory: " + ", ".join(bad))
     os.replace(tmp, out)
     return out
 

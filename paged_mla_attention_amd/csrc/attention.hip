@@ -163,7 +163,13 @@ struct Attn {
   // at most kMaxItemTiles tiles, so at most that many pages.
   static constexpr int kPageOff = kPOff + 2 * kPBufBytes;
   static constexpr int kPageLoads = (kMaxItemTiles + NW * kWave - 1) / (NW * kWave);
-  static constexpr int kLdsBytes = kPageOff + (kTileInPage ? kMaxItemTiles * 4 : 16);
+  // Tiles that may span pages: each wave keeps the page ids of its lanes'
+  // keys for kIdSlots tiles (32 ids of 4 bytes per tile), DMA'd kIdAhead
+  // tiles ahead of their use.
+  static constexpr int kIdSlots = 8;
+  static constexpr int kIdAhead = 4;
+  static constexpr int kIdWaveBytes = kIdSlots * kTileKeys * 4;
+  static constexpr int kLdsBytes = kPageOff + (kTileInPage ? kMaxItemTiles * 4 : NW * kIdWaveBytes);
   static_assert(kLdsBytes <= 160 * 1024, "LDS holds 160 KiB");
   // Output staging in the idle stages: per wave, 32 head rows of its columns.
   static constexpr int kFinRow = kDimBlocks * 32 + 4;  // floats (padding staggers banks)
@@ -231,21 +237,29 @@ struct Attn {
     return reinterpret_cast<const int*>(smem + kPageOff)[i];
   }
 
-  // Page id for the lane's own key `key` of the tile starting at `base`
-  // when a tile can span pages: 32 scalar loads and a select (a vector load
-  // here would make the in-order vmcnt wait for every DMA in flight).
-  __device__ __forceinline__ int lane_page(int base, int key) const {
-    const int P = a.page_size;
-    const_i32_t* idx = (const_i32_t*)(a.kv_indices) + page_base;
-    const int first = base / P;
-    const int j = key / P - first;  // 0 .. 31
-    int v = __builtin_amdgcn_readfirstlane(idx[first]);
-#pragma unroll
-    for (int i = 1; i < kTileKeys; ++i) {
-      const int pi = __builtin_amdgcn_readfirstlane(idx[first + i]);
-      v = (j == i) ? pi : v;
+  // Tiles that may span pages: the page id of key k (0 .. 31) of tile t sits
+  // in this wave's LDS ring at slot t % kIdSlots.  stage_ids(t) DMAs them
+  // there (lanes 0 .. 31, one 4-byte id each; keys past the item's end take
+  // its last key's page); the wave reads them kIdAhead tiles later.
+  __device__ __forceinline__ uint32_t id_slot_addr(int t) const {
+    return lds_base + kPageOff + wave * kIdWaveBytes + (t % kIdSlots) * (kTileKeys * 4);
+  }
+  __device__ __forceinline__ void stage_ids(int t) const {
+    if (lane < kTileKeys) {
+      const int P = a.page_size;
+      const int key = min(kv_begin + t * kTileKeys + lane, kv_end - 1);
+      const int pidx = P == 1 ? key : key / P;
+      const char* src = reinterpret_cast<const char*>(a.kv_indices + page_base + pidx);
+      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                   :
+                   : "v"(src), "s"(__builtin_amdgcn_readfirstlane(id_slot_addr(t)))
+                   : "m0");
     }
-    return v;
+  }
+  __device__ __forceinline__ int lane_page(int t, int k) const {
+    const int* ring = reinterpret_cast<const int*>(smem + kPageOff + wave * kIdWaveBytes +
+                                                   (t % kIdSlots) * (kTileKeys * 4));
+    return ring[k];
   }
 
   // One 16-byte-per-lane DMA from global memory into LDS at
@@ -313,14 +327,23 @@ struct Attn {
       d.src_e = d.src_o = nullptr;
     } else {
       const int P = a.page_size;
-      int ke = base + ld_key, ko = base + (ld_key ^ kSwzB);
-      ke = ke < kv_end ? ke : kv_end - 1;
-      ko = ko < kv_end ? ko : kv_end - 1;
-      const int pe = lane_page(base, ke), po = lane_page(base, ko);
-      d.src_e = reinterpret_cast<const char*>(
-          a.kv_cache + (static_cast<int64_t>(pe) * P + ke % P) * kLatentDim) + ld_off + wave * 32;
-      d.src_o = reinterpret_cast<const char*>(
-          a.kv_cache + (static_cast<int64_t>(po) * P + ko % P) * kLatentDim) + ld_off + wave * 32;
+      const int rem = kv_end - 1 - base;  // keys past the item's end re-read its last key
+      auto row_src = [&](int key) {
+        const int k = min(key, rem);
+        const int pg = lane_page(t, k);
+        const int r = P == 1 ? pg : pg * P + (base + k) % P;
+        return reinterpret_cast<const char*>(a.kv_cache + static_cast<int64_t>(r) * kLatentDim) +
+               ld_off + wave * 32;
+      };
+      // With several waves each wave loads one of the two key orders only
+      // (chosen here: a select between the two in front of every DMA ends
+      // up as a load from the stack).
+      if (NW == 1) {
+        d.src_e = row_src(ld_key);
+        d.src_o = row_src(ld_key ^ kSwzB);
+      } else {
+        d.src_e = d.src_o = row_src((wave & 1) ? (ld_key ^ kSwzB) : ld_key);
+      }
       d.sbase = nullptr;
       d.voff_e = d.voff_o = 0;
     }
@@ -340,7 +363,7 @@ struct Attn {
     if (kTileInPage)
       dma16s<kOff, kM0>(odd ? d.voff_o : d.voff_e, d.sbase, dbase);
     else
-      dma16<kOff, kM0>(odd ? d.src_o : d.src_e, dbase);
+      dma16<kOff, kM0>(NW == 1 && (j & 1) ? d.src_o : d.src_e, dbase);
   }
 
   template <int j0, int j1>
@@ -356,9 +379,12 @@ struct Attn {
     issue_range<0, kLoadsPerWave>(d);
   }
 
-  // Waits for this wave's DMAs except those of the newest tile if `later`.
-  __device__ __forceinline__ static void wait_vm(bool later) {
-    if (later) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerWave));
+  // Waits for this wave's DMAs except, if `later`, those issued in the
+  // previous iteration: the newest tile's and, if `later_id`, one page-id
+  // DMA.
+  __device__ __forceinline__ static void wait_vm(bool later, bool later_id) {
+    if (later && later_id) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerWave + 1));
+    else if (later) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerWave));
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   }
 
@@ -448,6 +474,13 @@ struct Attn {
             ++cur_pl;
           }
         };
+        if (!kTileInPage) {
+          // The first tiles' page ids; this wave reads only its own ring.
+#pragma unroll
+          for (int t = 0; t < kIdAhead; ++t)
+            if (t < ntiles) stage_ids(t);
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // (the ring reads stay below)
+        }
 #pragma unroll
         for (int t = 0; t < kTilesAhead; ++t)
           if (t < ntiles) {
@@ -458,17 +491,16 @@ struct Attn {
         int pg_next = kTileInPage ? page_at(min(cur_pl, n_pages - 1)) : 0;
         // Tile t: S(t), with the DMAs of tile t+2 between its k-steps; the
         // softmax of S(t); P(t) published in LDS; this wave's columns of
-        // P(t) . V(t) for every head.  With several waves and tiles that
-        // never span pages, the tiles are software-pipelined: P . V of tile
-        // t-1 runs after S(t), with the softmax of S(t) placed between its
-        // MFMAs, and one barrier per tile serves both (tile t has landed,
-        // P(t-1) is complete, every wave is done with tile t-2's stage and
-        // tile t-1's kpe slot).  The other kernels (one wave, or tiles that
-        // span pages, whose DMA set-up takes more registers) keep the
-        // unpipelined order with a second barrier before P . V.
-        constexpr bool kPipe = kTileInPage && NW > 1;
+        // P(t) . V(t) for every head.  With several waves the tiles are
+        // software-pipelined: P . V of tile t-1 runs after S(t), with the
+        // softmax of S(t) placed between its MFMAs, and one barrier per tile
+        // serves both (tile t has landed, P(t-1) is complete, every wave is
+        // done with tile t-2's stage and tile t-1's kpe slot).  A lone wave
+        // has no registers for that and keeps the unpipelined order with a
+        // second barrier before P . V.
+        constexpr bool kPipe = NW > 1;
         for (int t = 0; t < ntiles; ++t) {
-          wait_vm(t + 1 < ntiles);
+          wait_vm(t + 1 < ntiles, !kTileInPage && t + kIdAhead - 1 < ntiles);
           lds_barrier();
           const bool dma = t + kTilesAhead < ntiles;
           const int base = kv_begin + t * kTileKeys;
@@ -481,6 +513,8 @@ struct Attn {
               if (kTileInPage) {
                 advance();
                 pg_next = page_at(min(cur_pl, n_pages - 1));
+              } else if (t + kIdAhead < ntiles) {
+                stage_ids(t + kIdAhead);
               }
             };
             // With several waves, the DMA set-up goes under the first
