@@ -500,7 +500,9 @@ struct Attn {
         // second barrier before P . V.
         constexpr bool kPipe = NW > 1;
         for (int t = 0; t < ntiles; ++t) {
-          wait_vm(t + 1 < ntiles, !kTileInPage && t + kIdAhead - 1 < ntiles);
+          // (iteration t-1 staged the ids of tile t-1+kIdAhead, if any; the
+          // prologue stages none after its tiles)
+          wait_vm(t + 1 < ntiles, !kTileInPage && t > 0 && t + kIdAhead - 1 < ntiles);
           lds_barrier();
           const bool dma = t + kTilesAhead < ntiles;
           const int base = kv_begin + t * kTileKeys;
