@@ -244,22 +244,74 @@ struct Attn {
   __device__ __forceinline__ uint32_t id_slot_addr(int t) const {
     return lds_base + kPageOff + wave * kIdWaveBytes + (t % kIdSlots) * (kTileKeys * 4);
   }
+  // One 4-byte-per-lane DMA: lane i's word lands at LDS dst + 4 i.
+  __device__ __forceinline__ static void dma4(const int32_t* src, uint32_t dst) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(src), "s"(__builtin_amdgcn_readfirstlane(dst))
+                 : "m0");
+  }
   __device__ __forceinline__ void stage_ids(int t) const {
     if (lane < kTileKeys) {
       const int P = a.page_size;
       const int key = min(kv_begin + t * kTileKeys + lane, kv_end - 1);
-      const int pidx = P == 1 ? key : key / P;
-      const char* src = reinterpret_cast<const char*>(a.kv_indices + page_base + pidx);
-      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-                   :
-                   : "v"(src), "s"(__builtin_amdgcn_readfirstlane(id_slot_addr(t)))
-                   : "m0");
+      dma4(a.kv_indices + page_base + (P == 1 ? key : key / P), id_slot_addr(t));
+    }
+  }
+  // The item's page list (tiles that never span pages): entry i of its n
+  // pages at LDS kPageOff + 4 i, by DMA (lanes past the end re-read entry
+  // n-1).
+  __device__ __forceinline__ void stage_pages(int n) const {
+#pragma unroll
+    for (int k = 0; k < kPageLoads; ++k) {
+      const int i0 = (k * NW + wave) * kWave;  // this wave's first entry
+      if (i0 < n)
+        dma4(a.kv_indices + page_base + first_page + min(i0 + lane, n - 1),
+             lds_base + kPageOff + i0 * 4);
     }
   }
   __device__ __forceinline__ int lane_page(int t, int k) const {
     const int* ring = reinterpret_cast<const int*>(smem + kPageOff + wave * kIdWaveBytes +
                                                    (t % kIdSlots) * (kTileKeys * 4));
     return ring[k];
+  }
+
+  // Query staging.  Wave w's 32 heads (32 w .. 32 w + 31; heads past H
+  // take head 0's row) land at LDS offset w * kQWaveBytes: the q_nope row of
+  // head r at r * 1024, its q_pe row at 32 KiB + r * 128.  One DMA moves a
+  // whole q_nope row (64 lanes x 16 bytes) or eight whole q_pe rows, so each
+  // load reads full cache lines.  Within a row the 16-byte pieces are
+  // permuted (slot c holds piece c ^ (r % 16), q_pe: c ^ (r % 8)) so that
+  // the operand reads below, one head per lane, fall in distinct banks.
+  static constexpr int kQWaveBytes = 32 * kLatentDim * 2;
+  static_assert(NW * kQWaveBytes <= kPageOff, "the query fits below the page list");
+  __device__ __forceinline__ void stage_query(int H) const {
+    const char* qn = reinterpret_cast<const char*>(a.q_nope + static_cast<int64_t>(token) * H * kLoraRank);
+    const char* qp = reinterpret_cast<const char*>(a.q_pe + static_cast<int64_t>(token) * H * kRopeDim);
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_base + wave * kQWaveBytes);
+    // (opaque: computed per item, not kept in 36 registers for the kernel)
+    const int lane = opaque(this->lane);
+    static_for<32>([&](auto jc) {  // q_nope rows
+      constexpr int r = decltype(jc)::value;
+      const int h = wave * 32 + r;
+      const uint32_t voff = (h < H ? h : 0) * (kLoraRank * 2) + ((lane ^ (r % 16)) * 16);
+      dma16s<0, r * 1024>(voff, qn, dst);
+    });
+    static_for<4>([&](auto jc) {  // 8 q_pe rows each
+      constexpr int j = decltype(jc)::value;
+      const int r = 8 * j + (lane >> 3);
+      const int h = wave * 32 + r;
+      const uint32_t voff = (h < H ? h : 0) * (kRopeDim * 2) + (((lane & 7) ^ (r % 8)) * 16);
+      dma16s<0, 32768 + j * 1024>(voff, qp, dst);
+    });
+  }
+  // LDS offset of this lane's query operand for k-step ks.
+  __device__ __forceinline__ int query_lds_off(int ks, int lane) const {
+    const int l32 = lane & 31, half = lane >> 5;
+    if (ks < kLoraRank / 16)
+      return wave * kQWaveBytes + l32 * 1024 + (((2 * ks + half) ^ (l32 % 16)) * 16);
+    const int kp = ks - kLoraRank / 16;
+    return wave * kQWaveBytes + 32768 + l32 * 128 + (((2 * kp + half) ^ (l32 % 8)) * 16);
   }
 
   // One 16-byte-per-lane DMA from global memory into LDS at
@@ -417,53 +469,39 @@ struct Attn {
         l_run = 0.f;
         m_seen = -INFINITY;
         if (ntiles == 0) break;
+        // Every wave is done with the previous item's (or attempt's) LDS.
+        lds_barrier();
+        // This wave's query rows go through LDS: whole rows per DMA, where
+        // loading them straight into the MFMA operand layout would touch
+        // 32 rows per load (see stage_query).  The page ids go out in the
+        // same wait, also by DMA: the item's page list (tiles that never
+        // span pages) or the first tiles' per-key ids (tiles that may).
+        stage_query(H);
+        int n_pages = 1;
+        if (kTileInPage) {
+          const int P = a.page_size;
+          first_page = kv_begin / P;
+          n_pages = (kv_end - 1) / P - first_page + 1;  // <= kMaxItemTiles
+          stage_pages(n_pages);
+        } else {
+#pragma unroll
+          for (int t = 0; t < kIdAhead; ++t)
+            if (t < ntiles) stage_ids(t);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // (the LDS reads stay below)
         // Query as the B operand of the 32x32x16 score MFMAs: lane (l32,
-        // half) holds head 32 wave + l32, dims 16 ks + 8 half .. +8.  Padding
-        // heads (beyond H) compute with head 0's row; their results are never
-        // stored.  Loaded first (a redo attempt loads them again) and complete
-        // before the first DMA of the item, so that no wait for them can land
-        // in the key loop, where it would also wait for DMAs in flight.
+        // half) holds head 32 wave + l32, dims 16 ks + 8 half .. +8.
         u32x4_t q[kQSteps];
         {
           const int qlane = opaque(lane);
-          const int h = wave * 32 + (qlane & 31);
-          const int hq = h < H ? h : 0;
-          const uint16_t* qn = a.q_nope + (static_cast<int64_t>(token) * H + hq) * kLoraRank;
-          const uint16_t* qp = a.q_pe + (static_cast<int64_t>(token) * H + hq) * kRopeDim;
-          const int dl = 8 * (qlane >> 5);
 #pragma unroll
           for (int ks = 0; ks < kQSteps; ++ks)
-            q[ks] = ks < kLoraRank / 16
-                        ? *reinterpret_cast<const u32x4_t*>(qn + ks * 16 + dl)
-                        : *reinterpret_cast<const u32x4_t*>(qp + (ks - kLoraRank / 16) * 16 + dl);
+            q[ks] = *reinterpret_cast<const u32x4_t*>(smem + query_lds_off(ks, qlane));
         }
-        int n_pages = 1;
-        if (kTileInPage) {
-          // Stage the item's page ids in LDS; the loads go out before the
-          // barrier that waits for the previous item's LDS users.
-          const int P = a.page_size;
-          first_page = kv_begin / P;
-          const int n = (kv_end - 1) / P - first_page + 1;  // <= kMaxItemTiles
-          n_pages = n;
-          int pv[kPageLoads];
-#pragma unroll
-          for (int k = 0; k < kPageLoads; ++k) {
-            const int i = threadIdx.x + k * NW * kWave;
-            pv[k] = i < n ? reinterpret_cast<const int32_t*>(a.kv_indices)[page_base + first_page + i] : 0;
-          }
-          lds_barrier();
-          int* pl = reinterpret_cast<int*>(smem + kPageOff);
-#pragma unroll
-          for (int k = 0; k < kPageLoads; ++k) {
-            const int i = threadIdx.x + k * NW * kWave;
-            if (i < n) pl[i] = pv[k];
-          }
-        }
-        // The query rows have landed (the previous item's DMAs all have).
 #pragma unroll
         for (int ks = 0; ks < kQSteps; ++ks) asm volatile("" : : "v"(q[ks]));
-        // Every wave is done with the previous item's (or attempt's) LDS,
-        // and the page list is complete.
+        // Every wave has its query in registers, and the page list is
+        // complete.
         lds_barrier();
         // Page-list cursor: entry and first row of the next tile to load.
         int cur_pl = 0, cur_inp = kTileInPage ? kv_begin % a.page_size : 0;
@@ -474,13 +512,6 @@ struct Attn {
             ++cur_pl;
           }
         };
-        if (!kTileInPage) {
-          // The first tiles' page ids; this wave reads only its own ring.
-#pragma unroll
-          for (int t = 0; t < kIdAhead; ++t)
-            if (t < ntiles) stage_ids(t);
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // (the ring reads stay below)
-        }
 #pragma unroll
         for (int t = 0; t < kTilesAhead; ++t)
           if (t < ntiles) {
