@@ -3,7 +3,8 @@
 
 One step = one pass of the whole path over one batch: ``mla_plan`` (host
 planning, schedule staged for the device) and ``mla_run`` (attention kernel
-+ split-KV merge kernel); the plan of step k+1 is made while run k executes.  The workload is the decode batch
++ split-KV merge kernel); the plan of step k+1 is made while run k executes.
+The workload is the decode batch
 of 64 rows, 128 heads, page_size 64, kv lengths uniform in [512, 4096]
 (seed 1002), with inputs resident in HBM.  Three independent copies of the KV
 cache, queries and outputs are rotated so the 256 MB last-level cache cannot
@@ -110,29 +111,27 @@ def run_steps(w, steps, warmup, copies=3):
                   num_cache_pages=w.num_pages)
 
     # A step is one plan and one run.  As in a serving loop, the plan of the
-    # next step is made while this step's kernels run (its upload overlaps
-    # them); the run events time the kernels.
-    def step(k, ev=None):
+    # next step is made while this step's kernels run.  One pair of events on
+    # the launch stream brackets the timed steps (events between the steps
+    # would put their own markers between the kernels).
+    def step(k):
         c = k % copies
-        if ev is not None:
-            ev[0].record()
         plan.run(qns[c], qps[c], kvs[c], out=outs[c], lse=lses[c])
-        if ev is not None:
-            ev[1].record()
         do_plan()
 
     do_plan()
     for k in range(warmup):
         step(k)
     torch.cuda.synchronize()
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e0.record()
     for k in range(steps):
-        step(k, events[k])
+        step(k)
+    e1.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    run_ms = float(np.mean([a.elapsed_time(b) for a, b in events]))
+    run_ms = e0.elapsed_time(e1) / steps
     stats = plan.stats()
     plan.close()
     return wall * 1e3, run_ms, stats

@@ -25,13 +25,11 @@ __device__ __forceinline__ float bf16_hi(unsigned w) {
 }
 
 // Split-KV partials -> final bf16 output + LSE.  A piece k holds its
-// normalised output o_k (bf16) and its LSE s_k.  One block of 128 threads
-// per (merge entry, head); each thread owns 4 consecutive latent columns.
-// One wave per (merge item, head): lane l owns columns 8l .. 8l+7.  The
-// slots' LSEs are read lane-parallel for their maximum; then the partial
-// rows go out in batches of kBatch independent loads (with the slot LSEs as
-// uniform loads), so a token split in n pieces waits about n / kBatch load
-// latencies instead of n.
+// normalised output o_k (bf16) and its LSE s_k.  One wave per (merge item,
+// head): lane l owns columns 8l .. 8l+7.  The first batch of partial rows is
+// loaded together with the pieces' LSEs (lane k holds s_k), so a token split
+// in at most kBatch pieces costs one memory round trip; the weights come
+// from the LSE lanes by readlane.
 __global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeArgs a) {
   constexpr int kBatch = 8;
   const int lane = threadIdx.x & 63;
@@ -42,22 +40,37 @@ __global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeArgs a) {
   const MergeItem m = a.merges[mi];
   const int n = m.num_slots;
   const int64_t base = static_cast<int64_t>(m.first_slot) * H + h;  // slot k: base + k H
-  float M = -INFINITY;
-  for (int k = lane; k < n; k += 64) M = fmaxf(M, a.part_lse[base + static_cast<int64_t>(k) * H]);
+  const uint16_t* rows = a.part_o + base * kLoraRank + lane * 8;
+  const int64_t row_step = static_cast<int64_t>(H) * kLoraRank;
+  // Issued together: the first batch of rows and the LSEs of pieces 0..63.
+  u32x4_t r[kBatch];
+#pragma unroll
+  for (int b = 0; b < kBatch; ++b) {
+    const int k = b < n ? b : n - 1;  // (a repeated row gets weight 0)
+    r[b] = *reinterpret_cast<const u32x4_t*>(rows + k * row_step);
+  }
+  const float s_lane = lane < n ? a.part_lse[base + static_cast<int64_t>(lane) * H] : -INFINITY;
+  float M = s_lane;
+  for (int k = lane + 64; k < n; k += 64) M = fmaxf(M, a.part_lse[base + static_cast<int64_t>(k) * H]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
   if (M != -INFINITY) {
     for (int k0 = 0; k0 < n; k0 += kBatch) {
-      u32x4_t r[kBatch];
       float s[kBatch];
+      if (k0 > 0) {
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+          const int k = k0 + b < n ? k0 + b : n - 1;
+          r[b] = *reinterpret_cast<const u32x4_t*>(rows + k * row_step);
+        }
+      }
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
-        const int k = k0 + b < n ? k0 + b : n - 1;  // (a repeated slot gets weight 0)
-        const int64_t sh = base + static_cast<int64_t>(k) * H;
-        s[b] = a.part_lse[sh];
-        r[b] = *reinterpret_cast<const u32x4_t*>(a.part_o + sh * kLoraRank + lane * 8);
+        const int k = k0 + b;
+        s[b] = k < 64 ? __shfl(s_lane, k < n ? k : 0)
+                      : a.part_lse[base + static_cast<int64_t>(k < n ? k : n - 1) * H];
       }
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
