@@ -5,6 +5,7 @@ benchmark's CPU-baseline leg, never by the library itself.
 """
 
 from .mla_oracle import (  # noqa: F401
+    append_kv,
     attention,
     attention_loops,
     gather_row_keys,

@@ -34,6 +34,14 @@ row with Q queries sees keys ``j < min(L, i + L - Q + 1)`` when causal, all
 ``lse = -inf``; the LSE is over the *scaled* scores; ``sm_scale`` is used
 at the fp32 value the kernel receives.
 
+Appending the step's latent rows (page "mstar.engine.resources.attn.base",
+``AttentionManager.requires_kv_write``: a layer writes this step's K/V through
+the KV resource, then runs attention over the cache): reading, the step's Q
+tokens of a row are its last Q keys (the same end alignment as the causal
+query block; the page on ``kv_len_buf`` says a row's queries and the entries
+the step appends start at the end of its stored context), so token i of the
+row is key ``L - Q + i``.
+
 Parity pins: every function here is checked by the CPU tests against
 something other than itself (brute-force non-absorbed attention, page
 permutation invariance, the two-segment merge identity, the single-key and
@@ -239,3 +247,40 @@ def attention_loops(q_nope, q_pe, kv_cache, qo_indptr, kv_indptr, kv_indices,
                 o[t][h] = [a / z for a in acc]
                 lse[t][h] = m + math.log(z)
     return np.array(o, dtype=np.float64), np.array(lse, dtype=np.float64)
+
+
+def append_kv(kv_cache, ckv, kpe, qo_indptr, kv_indptr, kv_indices, kv_last_page_len,
+              page_size):
+    """The cache after this step's latent rows are written (a new array).
+
+    ``kv_cache`` is uint16 bf16 bits ``[pages, page_size, 576]``; ``ckv``
+    ``[T, 512]`` and ``kpe`` ``[T, 64]`` hold the step's rows for the tokens
+    of ``qo_indptr``.  Token ``t = qo_indptr[b] + i`` becomes key
+    ``j = L_b - Q_b + i`` of row b: ``[ckv[t] | kpe[t]]`` is stored at slot
+    ``j % page_size`` of page ``kv_indices[kv_indptr[b] + j // page_size]``.
+    Raises ValueError when a row has more tokens than keys, or when two
+    tokens would land in the same slot.
+    """
+    cache = np.array(kv_cache, copy=True)
+    num_pages = cache.shape[0]
+    validate(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, page_size, num_pages)
+    qo = np.asarray(qo_indptr, dtype=np.int64)
+    lens = kv_lengths(kv_indptr, kv_last_page_len, page_size)
+    idx = np.asarray(kv_indices, dtype=np.int64)
+    written = set()
+    for b in range(qo.shape[0] - 1):
+        Q = int(qo[b + 1] - qo[b])
+        L = int(lens[b])
+        if Q > L:
+            raise ValueError(f"row {b} has {Q} tokens but only {L} keys")
+        for i in range(Q):
+            j = L - Q + i
+            page = int(idx[int(kv_indptr[b]) + j // page_size])
+            slot = j % page_size
+            if (page, slot) in written:
+                raise ValueError(f"two tokens write page {page} slot {slot}")
+            written.add((page, slot))
+            t = int(qo[b]) + i
+            cache[page, slot, :KV_LORA_RANK] = ckv[t]
+            cache[page, slot, KV_LORA_RANK:] = kpe[t]
+    return cache
