@@ -192,7 +192,41 @@ def other_workloads(steps):
                           "frac": round(mbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                           "algorithmic_bytes": mbytes}
     print("[bench] mixed batch, extra segment and merge done", file=sys.stderr, flush=True)
+    out["append_kv"] = [append_kv_entry(W.decode_batch()), append_kv_entry(W.chunked_prefill())]
+    print("[bench] KV append done", file=sys.stderr, flush=True)
     return out
+
+
+def append_kv_entry(w, n=20):
+    """mla_append_kv for the workload's tokens: the step's new latent rows
+    written into their cache slots (1152 B read + 1152 B written per token,
+    plus its 4-byte destination), HBM-bound."""
+    import torch
+
+    import paged_mla_attention_amd as pm
+    rng = np.random.default_rng(7)
+    T = w.num_tokens
+    ckv = _to_dev_bf16(W.bf16_normals(rng, (T, 512)), torch)
+    kpe = _to_dev_bf16(W.bf16_normals(rng, (T, 64)), torch)
+    kv = _to_dev_bf16(w.kv_cache, torch)
+    plan = pm.MLAPlan(w.num_heads, w.page_size)
+    plan.plan(w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_len, causal=w.causal,
+              sm_scale=w.sm_scale, num_cache_pages=w.num_pages)
+    for _ in range(3):
+        plan.append_kv(ckv, kpe, kv)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        plan.append_kv(ckv, kpe, kv)
+    e1.record()
+    torch.cuda.synchronize()
+    plan.close()
+    ms = e0.elapsed_time(e1) / n
+    nbytes = T * (2 * 1152 + 4)
+    return {"workload": f"append_kv {w.name} T={T}", "run_ms": round(ms, 4),
+            "GB_s": round(nbytes / (ms * 1e-3) / 1e9, 1), "bound": "hbm",
+            "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes}
 
 
 def cpu_baseline(w, target_s=10.0):

@@ -126,6 +126,28 @@ mla_status mla_plan(mla_plan_t plan, const int32_t* qo_indptr, const int32_t* kv
 mla_status mla_run(mla_plan_t plan, const void* q_nope, const void* q_pe,
                    const void* kv_cache, void* out, float* lse, mla_stream_t stream);
 
+/* Write this step's latent rows into the cache before attention reads it
+ * (page "mstar.engine.resources.attn.base", AttentionManager.requires_kv_write:
+ * a layer writes the step's K/V through the KV resource, then calls run).
+ * Uses the planned page table: the Q query tokens of row b are the row's
+ * last Q keys, so token t = qo_indptr[b] + i becomes key j = L_b - Q_b + i
+ * and its row [ckv[t,:] | kpe[t,:]] is stored at slot j % page_size of page
+ * kv_indices[kv_indptr[b] + j / page_size] (the same end alignment as the
+ * causal query block).  Other slots are untouched.
+ *   ckv bf16 [T, 512], kpe bf16 [T, 64]: device memory, read;
+ *   kv_cache bf16 [num_cache_pages, page_size, 576]: device memory, written
+ *   in place (ckv into columns 0..511, kpe into 512..575).
+ * Enqueued on `stream` (one kernel; no allocation or synchronisation); call
+ * it before mla_run on the same stream.  Like mla_run it reads the plan's
+ * schedule, so the same re-planning fence applies.
+ *
+ * Errors: MLA_E_STATE without a successful mla_plan; MLA_E_INVALID for a NULL
+ * pointer (with T > 0), a row with more query tokens than keys, or two tokens
+ * that would land in the same cache slot (rows sharing pages); MLA_E_HIP if
+ * the launch fails. */
+mla_status mla_append_kv(mla_plan_t plan, const void* ckv, const void* kpe, void* kv_cache,
+                         mla_stream_t stream);
+
 /* Merge two attention results over disjoint key segments of the same
  * queries through their LSEs (FlashInferMLAManager.run: the LSE is returned
  * for merging with another key segment):
@@ -187,6 +209,13 @@ void mla_schedule_sizes(mla_schedule_t s, int32_t* num_workers, int64_t* num_ite
  * merges [num_merges*4] (host memory, sized from mla_schedule_sizes). */
 void mla_schedule_copy(mla_schedule_t s, int32_t* worker_indptr, int32_t* items,
                        int32_t* merges);
+
+/* The cache row (page * page_size + slot) mla_append_kv writes for each of
+ * the schedule's T query tokens, into rows [T] (host memory; may be NULL to
+ * only validate).  MLA_E_INVALID, with the reason, when the page table cannot
+ * take an append (a row with more tokens than keys, or two tokens in one
+ * slot). */
+mla_status mla_schedule_append_rows(mla_schedule_t s, int32_t* rows);
 
 void mla_schedule_destroy(mla_schedule_t s);
 

@@ -24,8 +24,8 @@ KV_LORA_RANK = 512
 QK_ROPE_HEAD_DIM = 64
 
 __all__ = [
-    "MLAPlan", "mla_plan_create", "mla_plan", "mla_run", "mla_merge_state",
-    "mla_plan_destroy", "mla_plan_stats", "merge_state", "schedule", "library",
+    "MLAPlan", "mla_plan_create", "mla_plan", "mla_run", "mla_append_kv", "mla_merge_state",
+    "mla_plan_destroy", "mla_plan_stats", "merge_state", "schedule", "append_rows", "library",
 ]
 
 
@@ -108,6 +108,12 @@ def mla_run(handle: int, q_nope_ptr: int, q_pe_ptr: int, kv_cache_ptr: int, out_
                                    lse_ptr, stream))
 
 
+def mla_append_kv(handle: int, ckv_ptr: int, kpe_ptr: int, kv_cache_ptr: int,
+                  stream: int) -> None:
+    lib = library()
+    _native.check(lib, lib.mla_append_kv(handle, ckv_ptr, kpe_ptr, kv_cache_ptr, stream))
+
+
 def mla_merge_state(v_a: int, s_a: int, v_b: int, s_b: int, v_out: int, s_out: int,
                     num_tokens: int, num_heads: int, stream: int) -> None:
     lib = library()
@@ -188,6 +194,23 @@ class MLAPlan:
         mla_run(self._h, qn, qp, kv, op, lp, _stream_handle(stream))
         return (out, lse) if (return_lse or lp is not None) else out
 
+    def append_kv(self, ckv, kpe, kv_cache, stream=None) -> None:
+        """Write this step's latent rows (``ckv [T, 512]``, ``kpe [T, 64]``
+        bf16) into ``kv_cache`` in place: token i of a row with Q tokens and
+        L keys becomes the row's key L - Q + i (mirrors the KV write a layer
+        makes before ``run``)."""
+        import torch
+        if self._planned is None:
+            raise RuntimeError("append_kv() before plan()")
+        T, pages = self._planned
+        if kv_cache.dim() != 3 or kv_cache.shape[0] < pages:
+            raise ValueError(f"kv_cache must be [>= {pages}, page_size, 576]")
+        cp = _dev_ptr(ckv, "ckv", torch.bfloat16, (T, KV_LORA_RANK))
+        pp = _dev_ptr(kpe, "kpe", torch.bfloat16, (T, QK_ROPE_HEAD_DIM))
+        kv = _dev_ptr(kv_cache, "kv_cache", torch.bfloat16,
+                      (kv_cache.shape[0], self.page_size, KV_LORA_RANK + QK_ROPE_HEAD_DIM))
+        mla_append_kv(self._h, cp, pp, kv, _stream_handle(stream))
+
     def stats(self) -> dict:
         return mla_plan_stats(self._h)
 
@@ -253,3 +276,25 @@ def schedule(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, page_size: int,
     finally:
         lib.mla_schedule_destroy(h)
     return {"worker_indptr": wi, "items": items, "merges": merges, "num_slots": s.value}
+
+
+def append_rows(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, page_size: int,
+                num_cache_pages: int, lib_path: Optional[str] = None) -> np.ndarray:
+    """The cache row (page * page_size + slot) the KV append writes for each
+    query token, from the host planner; raises MLAError if the page table
+    cannot take an append."""
+    lib = _native.load(lib_path or _native.LIB_PATH, host_only=True)
+    qo, kv = _host_i32(qo_indptr), _host_i32(kv_indptr)
+    idx, last = _host_i32(kv_indices), _host_i32(kv_last_page_len)
+    if idx.size == 0:
+        idx = np.zeros(1, np.int32)
+    h = c_void_p()
+    _native.check(lib, lib.mla_schedule_build(ctypes.byref(h), _ptr(qo), _ptr(kv), _ptr(idx),
+                                              _ptr(last), qo.shape[0] - 1, 1, page_size,
+                                              num_cache_pages, 1, 1))
+    try:
+        rows = np.zeros(max(1, int(qo[-1])), np.int32)
+        _native.check(lib, lib.mla_schedule_append_rows(h, _ptr(rows)))
+    finally:
+        lib.mla_schedule_destroy(h)
+    return rows[:int(qo[-1])]

@@ -20,6 +20,7 @@ SIGNATURES = {
     "mla_plan": (c_int32, [c_void_p, _i32p, _i32p, _i32p, _i32p, c_int32, c_int32, c_float,
                            c_int64, c_void_p]),
     "mla_run": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "mla_append_kv": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "mla_merge_state": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_int64, c_int32, c_void_p]),
     "mla_plan_destroy": (None, [c_void_p]),
@@ -30,11 +31,12 @@ SIGNATURES = {
                                      c_int32, c_int32, c_int64, c_int32, c_int32]),
     "mla_schedule_sizes": (None, [c_void_p, _i32p, _i64p, _i64p, _i64p]),
     "mla_schedule_copy": (None, [c_void_p, _i32p, _i32p, _i32p]),
+    "mla_schedule_append_rows": (c_int32, [c_void_p, _i32p]),
     "mla_schedule_destroy": (None, [c_void_p]),
 }
 
 HOST_ONLY = ("mla_status_str", "mla_last_error", "mla_schedule_build", "mla_schedule_sizes",
-             "mla_schedule_copy", "mla_schedule_destroy")
+             "mla_schedule_copy", "mla_schedule_append_rows", "mla_schedule_destroy")
 
 _cache = {}
 

@@ -23,7 +23,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla.so")
 HOST_LIB = os.path.join(PKG, "libmla_host.so")
 
-HIP_SOURCES = ["planner.cpp", "capi.cpp", "attention.hip", "merge.hip"]
+HIP_SOURCES = ["planner.cpp", "capi.cpp", "attention.hip", "merge.hip", "append.hip"]
 ARCH = "gfx950"
 
 

@@ -1,0 +1,41 @@
+// KV append for gfx950: writes this step's latent rows into the paged cache
+// before attention runs over it (page "mstar.engine.resources.attn.base",
+// AttentionManager.requires_kv_write: a layer writes the step's K/V through
+// the KV resource, then calls run).  The host planner gives every query
+// token its cache row (page * page_size + slot of key L - Q + i of its row);
+// this kernel is a bandwidth-bound scatter of 1152-byte rows.
+#include "kernels.h"
+
+namespace mla {
+namespace {
+
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+
+// One wave per token: lanes 0..63 copy the 1024-byte ckv part in 16-byte
+// pieces, lanes 0..7 the 128-byte kpe part, to the token's cache row.
+__global__ __launch_bounds__(256) void append_kv_kernel(const uint16_t* ckv, const uint16_t* kpe,
+                                                        const int32_t* rows, uint16_t* cache,
+                                                        int64_t num_tokens) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= num_tokens) return;
+  const int lane = threadIdx.x & 63;
+  uint16_t* dst = cache + static_cast<int64_t>(rows[t]) * kLatentDim;
+  const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ckv + t * kLoraRank + lane * 8);
+  u32x4_t w{};
+  if (lane < kRopeDim / 8) w = *reinterpret_cast<const u32x4_t*>(kpe + t * kRopeDim + lane * 8);
+  *reinterpret_cast<u32x4_t*>(dst + lane * 8) = v;
+  if (lane < kRopeDim / 8) *reinterpret_cast<u32x4_t*>(dst + kLoraRank + lane * 8) = w;
+}
+
+}  // namespace
+
+hipError_t launch_append_kv(const uint16_t* ckv, const uint16_t* kpe, const int32_t* rows,
+                            uint16_t* cache, int64_t num_tokens, hipStream_t stream) {
+  if (num_tokens <= 0) return hipSuccess;
+  const int64_t blocks = (num_tokens + 3) / 4;
+  hipLaunchKernelGGL(append_kv_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                     ckv, kpe, rows, cache, num_tokens);
+  return hipGetLastError();
+}
+
+}  // namespace mla

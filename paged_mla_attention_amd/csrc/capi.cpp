@@ -66,7 +66,8 @@ struct mla_plan_s {
   mla::Schedule sched;
 
   // Pinned host staging slots and the device mirror: worker_indptr | items
-  // | merges | kv_indptr | kv_indices, each section 256-byte aligned.
+  // | merges | kv_indptr | kv_indices | append rows, each section 256-byte
+  // aligned.
   struct HostSlot {
     char* h_stage = nullptr;
     size_t cap = 0;
@@ -78,7 +79,8 @@ struct mla_plan_s {
   bool direct = false;      // the kernels read the schedule from the host slot
   char* d_stage = nullptr;
   size_t d_stage_cap = 0;
-  size_t off_items = 0, off_merges = 0, off_kv_indptr = 0, off_kv_indices = 0;
+  size_t off_items = 0, off_merges = 0, off_kv_indptr = 0, off_kv_indices = 0, off_append = 0;
+  int append_checked = 0;  // 0: not yet, 1: no slot collision, -1: rejected
 
   // Split-KV partials: fp32 raw o [slots, H, 512], then lse [slots, H], then
   // 1/l [slots, H].
@@ -175,7 +177,9 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
   const size_t off_merges = off_items + align_up(n_items);
   const size_t off_kvp = off_merges + align_up(n_merges);
   const size_t off_idx = off_kvp + align_up(n_kvp);
-  const size_t total = off_idx + align_up(n_idx_pad);
+  const size_t n_app = s.append_rows.size() * sizeof(int32_t);
+  const size_t off_app = off_idx + align_up(n_idx_pad);
+  const size_t total = off_app + align_up(n_app);
 
   // This plan's host slot: the last copy from it and the last run that read
   // it must be done before it is refilled.
@@ -226,6 +230,7 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
   if (n_merges) std::memcpy(h + off_merges, s.merges.data(), n_merges);
   if (s.batch > 0) std::memcpy(h + off_kvp, kv_indptr, n_kvp);
   if (n_idx) std::memcpy(h + off_idx, kv_indices, n_idx);
+  if (n_app) std::memcpy(h + off_app, s.append_rows.data(), n_app);
   std::memset(h + off_idx + n_idx, 0, n_idx_pad - n_idx);
   if (!direct) {
     // (Stream order keeps the copy behind the runs that read the device
@@ -243,6 +248,8 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
   p->off_merges = off_merges;
   p->off_kv_indptr = off_kvp;
   p->off_kv_indices = off_idx;
+  p->off_append = off_app;
+  p->append_checked = 0;
   p->scale_log2 = sm_scale * 1.44269504088896340736f;
   p->sched = std::move(s);
   p->planned = true;
@@ -298,6 +305,43 @@ mla_status mla_run(mla_plan_t p, const void* q_nope, const void* q_pe, const voi
     // The host slot is read by these kernels.  (Under stream capture a
     // replay reads it whenever it runs: the caller must not re-plan twice
     // while such a graph may still replay.)
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &cap);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+    if (cap == hipStreamCaptureStatusNone) {
+      e = hipEventRecord(sl.done, stream);
+      if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+      sl.pending = true;
+    }
+  }
+  return MLA_OK;
+}
+
+mla_status mla_append_kv(mla_plan_t p, const void* ckv, const void* kpe, void* kv_cache,
+                         mla_stream_t stream_) {
+  mla::clear_last_error();
+  if (!p) return fail(MLA_E_INVALID, "NULL plan");
+  if (!p->planned) return fail(MLA_E_STATE, "mla_append_kv before a successful mla_plan");
+  const auto& s = p->sched;
+  if (p->append_checked == 0) p->append_checked = mla::check_append(s) == MLA_OK ? 1 : -1;
+  if (p->append_checked < 0) {
+    (void)mla::check_append(s);  // (sets the message again)
+    return MLA_E_INVALID;
+  }
+  if (s.num_tokens == 0) return MLA_OK;
+  if (!ckv || !kpe || !kv_cache) return fail(MLA_E_INVALID, "NULL ckv, kpe or kv_cache");
+  DeviceGuard g(p->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  auto& sl = p->slot[p->cur];
+  const char* d = p->direct ? sl.h_stage : p->d_stage;
+  hipError_t e = mla::launch_append_kv(
+      static_cast<const uint16_t*>(ckv), static_cast<const uint16_t*>(kpe),
+      reinterpret_cast<const int32_t*>(d + p->off_append), static_cast<uint16_t*>(kv_cache),
+      s.num_tokens, stream);
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  if (p->direct) {
+    // The kernel reads the host slot (as mla_run does).
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     e = hipStreamIsCapturing(stream, &cap);
     if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");

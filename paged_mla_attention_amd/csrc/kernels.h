@@ -42,6 +42,10 @@ hipError_t launch_attention(const AttnArgs& a, int num_workers, hipStream_t stre
 // Combines the partial results of tokens whose keys were split.
 hipError_t launch_split_merge(const SplitMergeArgs& a, hipStream_t stream);
 
+// KV append: latent row of token t ([ckv[t] | kpe[t]]) to cache row rows[t].
+hipError_t launch_append_kv(const uint16_t* ckv, const uint16_t* kpe, const int32_t* rows,
+                            uint16_t* cache, int64_t num_tokens, hipStream_t stream);
+
 // Two-segment LSE merge (mla_merge_state).
 hipError_t launch_merge_state(const uint16_t* v_a, const float* s_a, const uint16_t* v_b,
                               const float* s_b, uint16_t* v_out, float* s_out,

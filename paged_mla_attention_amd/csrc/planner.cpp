@@ -182,6 +182,31 @@ mla_status build_schedule(const PlanArgs& a, Schedule* out) {
     }
   }
 
+  // KV append targets: the step's tokens are the last keys of their rows.
+  std::vector<int32_t> append_rows(static_cast<size_t>(T), 0);
+  std::string append_error;
+  for (int32_t b = 0; b < B && append_error.empty(); ++b) {
+    const int32_t n = a.kv_indptr[b + 1] - a.kv_indptr[b];
+    const int64_t L = n > 0 ? int64_t(n - 1) * a.page_size + a.kv_last_page_len[b] : 0;
+    const int32_t Q = a.qo_indptr[b + 1] - a.qo_indptr[b];
+    if (Q > L) {
+      std::snprintf(buf, sizeof buf, "row %d has %d query tokens but %lld keys: nowhere to append",
+                    b, Q, (long long)L);
+      append_error = buf;
+      break;
+    }
+    for (int32_t i = 0; i < Q; ++i) {
+      const int64_t j = L - Q + i;
+      const int64_t page = a.kv_indices[a.kv_indptr[b] + j / a.page_size];
+      const int64_t r = page * a.page_size + j % a.page_size;
+      if (r > INT32_MAX) {
+        append_error = "cache rows beyond 2^31 are not addressable by the append";
+        break;
+      }
+      append_rows[a.qo_indptr[b] + i] = static_cast<int32_t>(r);
+    }
+  }
+
   const CostModel cm(a.num_heads);
   double total = 0.0;
   for (const TokenWork& tw : toks) total += tw.tiles + cm.item;
@@ -246,12 +271,27 @@ mla_status build_schedule(const PlanArgs& a, Schedule* out) {
     s.worker_indptr[p + 1] = s.worker_indptr[p] + (first[l + 1] - first[l]);
     s.items.insert(s.items.end(), items.begin() + first[l], items.begin() + first[l + 1]);
   }
+  s.append_rows = std::move(append_rows);
+  s.append_error = std::move(append_error);
   s.num_workers = W;
   s.batch = B;
   s.num_tokens = T;
   s.num_slots = slots;
   s.nnz = nnz;
   *out = std::move(s);
+  return MLA_OK;
+}
+
+mla_status check_append(const Schedule& s) {
+  if (!s.append_error.empty()) return fail(MLA_E_INVALID, s.append_error);
+  std::vector<int32_t> rows(s.append_rows);
+  std::sort(rows.begin(), rows.end());
+  const auto dup = std::adjacent_find(rows.begin(), rows.end());
+  if (dup != rows.end()) {
+    char buf[128];
+    std::snprintf(buf, sizeof buf, "two query tokens append into cache row %d", *dup);
+    return fail(MLA_E_INVALID, buf);
+  }
   return MLA_OK;
 }
 
@@ -325,6 +365,16 @@ void mla_schedule_copy(mla_schedule_t s, int32_t* worker_indptr, int32_t* items,
     std::memcpy(items, s->s.items.data(), s->s.items.size() * sizeof(mla::WorkItem));
   if (merges && !s->s.merges.empty())
     std::memcpy(merges, s->s.merges.data(), s->s.merges.size() * sizeof(mla::MergeItem));
+}
+
+mla_status mla_schedule_append_rows(mla_schedule_t s, int32_t* rows) {
+  mla::clear_last_error();
+  if (!s) return mla::fail(MLA_E_INVALID, "NULL schedule");
+  const mla_status st = mla::check_append(s->s);
+  if (st != MLA_OK) return st;
+  if (rows && !s->s.append_rows.empty())
+    std::memcpy(rows, s->s.append_rows.data(), s->s.append_rows.size() * sizeof(int32_t));
+  return MLA_OK;
 }
 
 void mla_schedule_destroy(mla_schedule_t s) { delete s; }

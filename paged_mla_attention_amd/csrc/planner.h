@@ -65,7 +65,18 @@ struct Schedule {
   std::vector<int32_t> worker_indptr;  // [num_workers + 1], launch order
   std::vector<WorkItem> items;
   std::vector<MergeItem> merges;
+  // KV append: cache row (page * page_size + slot) of each query token's
+  // latent (token i of a row with Q tokens and L keys is key L - Q + i), and,
+  // if the page table cannot take an append, why.
+  std::vector<int32_t> append_rows;
+  std::string append_error;
 };
+
+// Checks that no two tokens of the schedule append into the same cache slot
+// (rows shared between requests may name the same pages).  Returns
+// MLA_E_INVALID, with the thread's last-error text set, on a collision or
+// when the schedule's append_error is set.
+mla_status check_append(const Schedule& s);
 
 // Validates `a` and fills `out`.  On failure returns the status, sets the
 // thread's last-error text and leaves `out` untouched.
