@@ -158,7 +158,7 @@ def other_workloads(steps):
     out = {}
     wl = W.long_decode()
     b, f = algorithmic(wl)
-    _, run_ms, stats = run_steps(wl, steps, 3, copies=1)
+    _, run_ms, stats = run_steps(wl, steps, 50, copies=1)
     out["long_decode"] = dict(roofline_entry(wl, run_ms, b, f), plan=stats)
     print(f"[bench] long decode: mla_run {run_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
 
@@ -317,8 +317,9 @@ def record_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # (a decode step is ~0.1 ms: 200 warm-up steps let the clocks settle)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-others", action="store_true",
@@ -350,7 +351,7 @@ def main():
 
     if args.prefill_only:
         wp = W.chunked_prefill()
-        p_ms, p_run_ms, _ = run_steps(wp, max(3, args.steps // 5), args.warmup, copies=1)
+        p_ms, p_run_ms, _ = run_steps(wp, max(3, min(args.steps // 5, 20)), min(args.warmup, 3), copies=1)
         print(f"[bench] prefill: {p_ms:.3f} ms/step, mla_run {p_run_ms:.3f} ms", file=sys.stderr,
               flush=True)
         return
@@ -370,7 +371,7 @@ def main():
         wp = W.chunked_prefill()
         pbytes, pflops = algorithmic(wp)
         print("[bench] prefill workload ready", file=sys.stderr, flush=True)
-        p_ms, p_run_ms, _ = run_steps(wp, max(3, args.steps // 5), 2, copies=1)
+        p_ms, p_run_ms, _ = run_steps(wp, max(3, min(args.steps // 5, 20)), 2, copies=1)
         prefill = {"workload": wp.name, "tflops": round(pflops / (p_ms * 1e-3) / 1e12, 2),
                    "run_tflops": round(pflops / (p_run_ms * 1e-3) / 1e12, 2),
                    "ms_per_step": round(p_ms, 4), "run_ms": round(p_run_ms, 4),
@@ -381,7 +382,7 @@ def main():
 
     others = None
     if not args.no_prefill and not args.no_others:
-        others = other_workloads(max(10, args.steps // 2))
+        others = other_workloads(max(10, min(args.steps // 2, 50)))
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -116,10 +116,13 @@ mla_status mla_plan(mla_plan_t plan, const int32_t* qo_indptr, const int32_t* kv
 
 /* Run the planned batch (FlashInferMLAWrapper.run): all pointers are device
  * memory with the layouts above; `lse` may be NULL when not wanted.  The call
- * only enqueues kernels on `stream`, and an event that later plans wait on
- * (no allocation, no synchronisation), so it may be captured in a HIP graph;
- * the event is left out under capture.  The plan must not be re-planned while
- * a captured graph that reads it may still replay.
+ * only enqueues kernels on `stream` (no allocation, no synchronisation), so
+ * it may be captured in a HIP graph.  A schedule read straight from its host
+ * slot is released by the kernels themselves (each workgroup stores the
+ * run's sequence number to pinned memory when it is done with the slot; a
+ * later mla_plan waits on those); all runs of one plan must therefore be
+ * ordered on one stream.  The plan must not be re-planned while a captured
+ * graph that reads it may still replay.
  *
  * Errors: MLA_E_STATE without a successful mla_plan; MLA_E_INVALID for a NULL
  * required pointer; MLA_E_HIP if a launch fails. */

@@ -14,12 +14,13 @@ typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
 // One wave per token: lanes 0..63 copy the 1024-byte ckv part in 16-byte
 // pieces, lanes 0..7 the 128-byte kpe part, to the token's cache row.
 __global__ __launch_bounds__(256) void append_kv_kernel(const uint16_t* ckv, const uint16_t* kpe,
-                                                        const int32_t* rows, uint16_t* cache,
+                                                        AppendRows rows, uint16_t* cache,
                                                         int64_t num_tokens) {
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= num_tokens) return;
   const int lane = threadIdx.x & 63;
-  uint16_t* dst = cache + static_cast<int64_t>(rows[t]) * kLatentDim;
+  const int32_t r = rows.rows ? rows.rows[t] : rows.inline_rows[t];
+  uint16_t* dst = cache + static_cast<int64_t>(r) * kLatentDim;
   const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ckv + t * kLoraRank + lane * 8);
   u32x4_t w{};
   if (lane < kRopeDim / 8) w = *reinterpret_cast<const u32x4_t*>(kpe + t * kRopeDim + lane * 8);
@@ -29,8 +30,9 @@ __global__ __launch_bounds__(256) void append_kv_kernel(const uint16_t* ckv, con
 
 }  // namespace
 
-hipError_t launch_append_kv(const uint16_t* ckv, const uint16_t* kpe, const int32_t* rows,
+hipError_t launch_append_kv(const uint16_t* ckv, const uint16_t* kpe, const AppendRows& rows,
                             uint16_t* cache, int64_t num_tokens, hipStream_t stream) {
+  if (!rows.rows && num_tokens > kInlineRows) return hipErrorInvalidValue;
   if (num_tokens <= 0) return hipSuccess;
   const int64_t blocks = (num_tokens + 3) / 4;
   hipLaunchKernelGGL(append_kv_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,

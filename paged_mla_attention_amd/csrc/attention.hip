@@ -441,6 +441,13 @@ struct Attn {
   }
 
   __device__ void run() {
+    if (a.merge_src) {  // each workgroup copies its share of the merge list
+      const int per = (a.merge_ints + static_cast<int>(gridDim.x) - 1) / static_cast<int>(gridDim.x);
+      for (int j = threadIdx.x; j < per; j += blockDim.x) {
+        const int i = static_cast<int>(blockIdx.x) * per + j;
+        if (i < a.merge_ints) a.merge_dst[i] = a.merge_src[i];
+      }
+    }
     const_i32_t* widx = (const_i32_t*)(a.worker_indptr);
     const int w_begin = widx[blockIdx.x];
     const int w_end = widx[blockIdx.x + 1];
@@ -609,6 +616,13 @@ struct Attn {
       }
       finish(o, m_ref, l_run);
     }
+    // Every read of the schedule (items, page lists, merge entries) has been
+    // consumed by every wave: tell the host this workgroup is done with the
+    // slot.
+    lds_barrier();
+    if (a.done_flags && threadIdx.x == 0)
+      __hip_atomic_store(a.done_flags + blockIdx.x, a.run_seq, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_SYSTEM);
   }
 
   __device__ __forceinline__ void store_p(const bf16x8_t (&p)[2], char* pb) const {

@@ -18,6 +18,7 @@
 #include <cstdio>
 #include <cstring>
 #include <new>
+#include <thread>
 
 #include "kernels.h"
 #include "planner.h"
@@ -73,6 +74,10 @@ struct mla_plan_s {
     size_t cap = 0;
     hipEvent_t done = nullptr;  // after the last copy from / run reading the slot
     bool pending = false;
+    // Runs that read the schedule straight from this slot: each attention
+    // workgroup stores the run's sequence number here when done with it.
+    int32_t* flags = nullptr;   // pinned [num_workers]
+    int32_t wait_seq = 0;       // > 0: wait for every flag to reach it
   };
   HostSlot slot[2];
   int cur = 0;              // slot of the current plan
@@ -81,6 +86,11 @@ struct mla_plan_s {
   size_t d_stage_cap = 0;
   size_t off_items = 0, off_merges = 0, off_kv_indptr = 0, off_kv_indices = 0, off_append = 0;
   int append_checked = 0;  // 0: not yet, 1: no slot collision, -1: rejected
+  int32_t run_seq = 0;     // sequence number of the last mla_run
+  // Merge entries of a schedule read from a host slot, copied here by the
+  // attention kernel for the merge kernel.
+  int32_t* d_merges = nullptr;
+  size_t merges_cap = 0;   // int32
 
   // Split-KV partials: fp32 raw o [slots, H, 512], then lse [slots, H], then
   // 1/l [slots, H].
@@ -91,12 +101,24 @@ struct mla_plan_s {
 
 namespace {
 
+// Waits until every attention workgroup of the run that last read `sl` from
+// the host has stored its sequence number (or a later one).
+void wait_flags(const mla_plan_s* p, mla_plan_s::HostSlot& sl) {
+  const volatile int32_t* f = sl.flags;
+  for (int w = 0; w < p->num_workers; ++w)
+    while (static_cast<int32_t>(f[w] - sl.wait_seq) < 0) std::this_thread::yield();
+  sl.wait_seq = 0;
+}
+
 void release(mla_plan_s* p) {
   for (auto& sl : p->slot) {
     if (sl.pending) (void)hipEventSynchronize(sl.done);
+    if (sl.wait_seq > 0) wait_flags(p, sl);
     if (sl.done) (void)hipEventDestroy(sl.done);
     if (sl.h_stage) (void)hipHostFree(sl.h_stage);
+    if (sl.flags) (void)hipHostFree(sl.flags);
   }
+  if (p->d_merges) (void)hipFree(p->d_merges);
   if (p->d_stage) (void)hipFree(p->d_stage);
   if (p->d_part) (void)hipFree(p->d_part);
   delete p;
@@ -137,6 +159,13 @@ mla_status mla_plan_create(mla_plan_t* out, int32_t device, int32_t num_heads,
       release(p);
       return hip_fail(e, "hipEventCreate");
     }
+    e = hipHostMalloc(reinterpret_cast<void**>(&sl.flags), p->num_workers * sizeof(int32_t),
+                      hipHostMallocCoherent);
+    if (e != hipSuccess) {
+      release(p);
+      return hip_fail(e, "hipHostMalloc(flags)");
+    }
+    std::memset(sl.flags, 0, p->num_workers * sizeof(int32_t));
   }
   *out = p;
   return MLA_OK;
@@ -191,6 +220,7 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
     if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
     sl.pending = false;
   }
+  if (sl.wait_seq > 0) wait_flags(p, sl);
   if (total > sl.cap) {
     if (sl.h_stage) (void)hipHostFree(sl.h_stage);
     sl.h_stage = nullptr;
@@ -203,7 +233,9 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
   // Partials: bf16 output rows [slots, H, 512] then fp32 LSE [slots, H].
   const size_t part_floats =
       static_cast<size_t>(s.num_slots) * p->num_heads * (mla::kLoraRank / 2 + 1);
-  if ((!direct && total > p->d_stage_cap) || part_floats > p->part_cap) {
+  const size_t merge_ints = direct ? s.merges.size() * 4 : 0;
+  if ((!direct && total > p->d_stage_cap) || part_floats > p->part_cap ||
+      merge_ints > p->merges_cap) {
     // Buffers may still be read by enqueued kernels of an earlier plan.
     e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
@@ -214,6 +246,14 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
       e = hipMalloc(reinterpret_cast<void**>(&p->d_stage), total);
       if (e != hipSuccess) return hip_fail(e, "hipMalloc(schedule)");
       p->d_stage_cap = total;
+    }
+    if (merge_ints > p->merges_cap) {
+      if (p->d_merges) (void)hipFree(p->d_merges);
+      p->d_merges = nullptr;
+      p->merges_cap = 0;
+      e = hipMalloc(reinterpret_cast<void**>(&p->d_merges), merge_ints * sizeof(int32_t));
+      if (e != hipSuccess) return hip_fail(e, "hipMalloc(merges)");
+      p->merges_cap = merge_ints;
     }
     if (part_floats > p->part_cap) {
       if (p->d_part) (void)hipFree(p->d_part);
@@ -287,32 +327,41 @@ mla_status mla_run(mla_plan_t p, const void* q_nope, const void* q_pe, const voi
   a.num_heads = p->num_heads;
   a.page_size = p->page_size;
   a.scale_log2 = p->scale_log2;
+  // A schedule read from the host slot: the attention workgroups report when
+  // they are done with it (no event between the kernels; runs of one plan
+  // are stream-ordered, so a slot's flags only grow), and the merge list
+  // reaches the merge kernel through device memory.
+  bool capturing = false;
+  if (p->direct) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    hipError_t ce = hipStreamIsCapturing(stream, &cap);
+    if (ce != hipSuccess) return hip_fail(ce, "hipStreamIsCapturing");
+    capturing = cap != hipStreamCaptureStatusNone;
+    a.done_flags = sl.flags;
+    a.run_seq = ++p->run_seq;
+    if (!s.merges.empty()) {
+      a.merge_src = reinterpret_cast<const int32_t*>(d + p->off_merges);
+      a.merge_dst = p->d_merges;
+      a.merge_ints = static_cast<int32_t>(s.merges.size() * 4);
+    }
+  }
   hipError_t e = mla::launch_attention(a, s.num_workers, stream);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
+  // (Under stream capture a replay reads the slot whenever it runs: the
+  // caller must not re-plan twice while such a graph may still replay.)
+  if (p->direct && !capturing) sl.wait_seq = a.run_seq;
   if (!s.merges.empty()) {
     mla::SplitMergeArgs m{};
     m.part_o = a.part_o;
     m.part_lse = a.part_lse;
-    m.merges = reinterpret_cast<const mla::MergeItem*>(d + p->off_merges);
+    m.merges = p->direct ? reinterpret_cast<const mla::MergeItem*>(p->d_merges)
+                         : reinterpret_cast<const mla::MergeItem*>(d + p->off_merges);
     m.out = a.out;
     m.lse = lse;
     m.num_heads = p->num_heads;
     m.num_merges = static_cast<int32_t>(s.merges.size());
     e = mla::launch_split_merge(m, stream);
     if (e != hipSuccess) return hip_fail(e, "split-merge launch");
-  }
-  if (p->direct) {
-    // The host slot is read by these kernels.  (Under stream capture a
-    // replay reads it whenever it runs: the caller must not re-plan twice
-    // while such a graph may still replay.)
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    e = hipStreamIsCapturing(stream, &cap);
-    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
-    if (cap == hipStreamCaptureStatusNone) {
-      e = hipEventRecord(sl.done, stream);
-      if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-      sl.pending = true;
-    }
   }
   return MLA_OK;
 }
@@ -335,12 +384,20 @@ mla_status mla_append_kv(mla_plan_t p, const void* ckv, const void* kpe, void* k
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   auto& sl = p->slot[p->cur];
   const char* d = p->direct ? sl.h_stage : p->d_stage;
-  hipError_t e = mla::launch_append_kv(
-      static_cast<const uint16_t*>(ckv), static_cast<const uint16_t*>(kpe),
-      reinterpret_cast<const int32_t*>(d + p->off_append), static_cast<uint16_t*>(kv_cache),
-      s.num_tokens, stream);
+  // A schedule staged in the host slot hands its few rows over as kernel
+  // arguments (nothing reads the slot); otherwise the kernel reads them from
+  // the device copy.
+  const bool inline_rows = p->direct && s.num_tokens <= mla::kInlineRows;
+  mla::AppendRows rows{};
+  if (inline_rows)
+    std::memcpy(rows.inline_rows, s.append_rows.data(), s.append_rows.size() * sizeof(int32_t));
+  else
+    rows.rows = reinterpret_cast<const int32_t*>(d + p->off_append);
+  hipError_t e = mla::launch_append_kv(static_cast<const uint16_t*>(ckv),
+                                       static_cast<const uint16_t*>(kpe), rows,
+                                       static_cast<uint16_t*>(kv_cache), s.num_tokens, stream);
   if (e != hipSuccess) return hip_fail(e, "append launch");
-  if (p->direct) {
+  if (p->direct && !inline_rows) {
     // The kernel reads the host slot (as mla_run does).
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     e = hipStreamIsCapturing(stream, &cap);

@@ -24,6 +24,24 @@ struct AttnArgs {
   int32_t num_heads;
   int32_t page_size;
   float scale_log2;  // sm_scale * log2(e)
+  // Schedule read from a pinned host slot: the merge entries (merge_ints
+  // int32) are copied to device memory for the merge kernel, and each
+  // workgroup stores run_seq to done_flags[workgroup] once it has read the
+  // slot for the last time (the host waits on these before refilling it).
+  const int32_t* merge_src;
+  int32_t* merge_dst;
+  int32_t merge_ints;
+  int32_t* done_flags;
+  int32_t run_seq;
+};
+
+// The append kernel's destination rows: a device/host array, or, for a few
+// tokens, the values themselves (kernel arguments need no memory read
+// ahead of the copy and leave the staging slot unread).
+constexpr int kInlineRows = 512;
+struct AppendRows {
+  const int32_t* rows;  // nullptr: use inline_rows
+  int32_t inline_rows[kInlineRows];
 };
 
 struct SplitMergeArgs {
@@ -43,7 +61,7 @@ hipError_t launch_attention(const AttnArgs& a, int num_workers, hipStream_t stre
 hipError_t launch_split_merge(const SplitMergeArgs& a, hipStream_t stream);
 
 // KV append: latent row of token t ([ckv[t] | kpe[t]]) to cache row rows[t].
-hipError_t launch_append_kv(const uint16_t* ckv, const uint16_t* kpe, const int32_t* rows,
+hipError_t launch_append_kv(const uint16_t* ckv, const uint16_t* kpe, const AppendRows& rows,
                             uint16_t* cache, int64_t num_tokens, hipStream_t stream);
 
 // Two-segment LSE merge (mla_merge_state).
