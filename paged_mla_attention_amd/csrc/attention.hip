@@ -440,6 +440,35 @@ struct Attn {
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   }
 
+  // This XCD's queue is empty: take an item from another queue.  The heads
+  // of all other queues are read at once (one round trip); a queue that
+  // still has items is then popped.  Returns -1 when every queue is empty.
+  // (Wave 0, lane 0 only.)
+  __device__ int steal() const {
+    const int qx = blockIdx.x % kXcds;
+    for (;;) {
+      int head[kXcds - 1];
+#pragma unroll
+      for (int k = 0; k < kXcds - 1; ++k)
+        head[k] = __hip_atomic_load(a.queue_ctr + (qx + 1 + k) % kXcds, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+      // Start the scan at a workgroup-dependent queue, so the workgroups of
+      // one XCD spread over the others.
+      int pick = -1;
+      const int s0 = (blockIdx.x / kXcds) % (kXcds - 1);
+#pragma unroll
+      for (int k = 0; k < kXcds - 1; ++k) {
+        const int kk = (s0 + k) % (kXcds - 1);
+        const int q = (qx + 1 + kk) % kXcds;
+        if (pick < 0 && head[kk] < a.queue_begin[q + 1] - a.queue_begin[q]) pick = q;
+      }
+      if (pick < 0) return -1;
+      const int i = __hip_atomic_fetch_add(a.queue_ctr + pick, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      if (i < a.queue_begin[pick + 1] - a.queue_begin[pick]) return a.queue_begin[pick] + i;
+    }
+  }
+
   __device__ void run() {
     if (a.merge_src) {  // each workgroup copies its share of the merge list
       const int per = (a.merge_ints + static_cast<int>(gridDim.x) - 1) / static_cast<int>(gridDim.x);
@@ -448,12 +477,36 @@ struct Attn {
         if (i < a.merge_ints) a.merge_dst[i] = a.merge_src[i];
       }
     }
+    const bool queued = a.queue_ctr != nullptr;
     const_i32_t* widx = (const_i32_t*)(a.worker_indptr);
-    const int w_begin = widx[blockIdx.x];
-    const int w_end = widx[blockIdx.x + 1];
+    const int w_begin = queued ? 0 : widx[blockIdx.x];
+    const int w_end = queued ? 0 : widx[blockIdx.x + 1];
     const int H = a.num_heads;
+    // Work queues: wave 0's lane 0 pops; the next pop from this XCD's queue
+    // is issued at the start of each item and read at the start of the next.
+    const int qx = blockIdx.x % kXcds;
+    int q_raw = 0;
+    if (queued && wave == 0 && lane == 0)
+      q_raw = __hip_atomic_fetch_add(a.queue_ctr + qx, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-    for (int it = w_begin; it < w_end; ++it) {
+    for (int it = w_begin;; ++it) {
+      if (queued) {
+        int* qw = reinterpret_cast<int*>(smem + kFlagOff) + 16;
+        if (wave == 0 && lane == 0) {
+          const int b = a.queue_begin[qx], len = a.queue_begin[qx + 1] - b;
+          const bool own = q_raw < len;
+          const int got = own ? b + q_raw : steal();
+          qw[0] = got;
+          if (own)
+            q_raw = __hip_atomic_fetch_add(a.queue_ctr + qx, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+        }
+        lds_barrier();
+        it = __builtin_amdgcn_readfirstlane(qw[0]);
+        if (it < 0) break;
+      } else if (it >= w_end) {
+        break;
+      }
       const_i32_t* item = (const_i32_t*)(a.items) + it * 8;  // WorkItem fields
       token = item[0];
       kv_begin = item[2];
@@ -615,6 +668,15 @@ struct Attn {
         m_ref = fmaxf(m_seen, __shfl_xor(m_seen, 32));  // the head's largest score
       }
       finish(o, m_ref, l_run);
+    }
+    if (queued && wave == 0 && lane == 0) {
+      // Every queue is empty for this workgroup; the last one out resets the
+      // counters for the next run (all other pops have returned by then).
+      const int d = __hip_atomic_fetch_add(a.queue_ctr + kXcds, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      if (d == static_cast<int>(gridDim.x) - 1)
+        for (int q = 0; q <= kXcds; ++q)
+          __hip_atomic_store(a.queue_ctr + q, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     // Every read of the schedule (items, page lists, merge entries) has been
     // consumed by every wave: tell the host this workgroup is done with the
