@@ -5,12 +5,15 @@ benchmark's CPU-baseline leg, never by the library itself.
 """
 
 from .mla_oracle import (  # noqa: F401
+    absorb_query,
     append_kv,
     attention,
     attention_loops,
     gather_row_keys,
+    head_matmul,
     kv_lengths,
     merge_state,
+    up_project,
     validate,
     visible_keys,
     widen,

@@ -42,6 +42,14 @@ query block; the page on ``kv_len_buf`` says a row's queries and the entries
 the step appends start at the end of its stored context), so token i of the
 row is key ``L - Q + i``.
 
+The projections either side of the kernel (module description of the
+flashinfer_mla page: the cache is the latent, the query is absorbed as
+``q_nope @ W_UK``, and the latent output is brought back to the value heads
+by ``W_UV``): per head, ``q_abs[t,h,:] = q_nope[t,h,:] @ W_UK[h]`` with
+``W_UK [H, d_nope, 512]`` and ``v[t,h,:] = o[t,h,:] @ W_UV[h]`` with
+``W_UV [H, 512, d_v]``; reading (the pages state only the 192-wide scale):
+``d_nope = d_v = 128``.
+
 Parity pins: every function here is checked by the CPU tests against
 something other than itself (brute-force non-absorbed attention, page
 permutation invariance, the two-segment merge identity, the single-key and
@@ -284,3 +292,25 @@ def append_kv(kv_cache, ckv, kpe, qo_indptr, kv_indptr, kv_indices, kv_last_page
             cache[page, slot, :KV_LORA_RANK] = ckv[t]
             cache[page, slot, KV_LORA_RANK:] = kpe[t]
     return cache
+
+
+def head_matmul(x, w):
+    """Per-head product ``out[t, h, :] = x[t, h, :] @ w[h]`` in fp64.
+
+    ``x [T, H, K]`` and ``w [H, K, N]`` are bf16 bit patterns (uint16) or
+    float arrays; returns ``[T, H, N]`` fp64.
+    """
+    xf, wf = widen(x), widen(w)
+    return np.einsum("thk,hkn->thn", xf, wf)
+
+
+def absorb_query(q_nope, w_uk):
+    """The absorbed query ``q_nope @ W_UK`` per head: ``[T, H, 128] x
+    [H, 128, 512] -> [T, H, 512]`` (fp64)."""
+    return head_matmul(q_nope, w_uk)
+
+
+def up_project(o, w_uv):
+    """The latent output brought to the value heads, ``o @ W_UV`` per head:
+    ``[T, H, 512] x [H, 512, 128] -> [T, H, 128]`` (fp64)."""
+    return head_matmul(o, w_uv)

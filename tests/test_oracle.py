@@ -62,11 +62,12 @@ def test_absorbed_equals_non_absorbed(page_size, kv_lens, qo_lens, causal):
     W_UV = rng.standard_normal((H, W.KV_LORA_RANK, d_v)) / math.sqrt(W.KV_LORA_RANK)
     q_orig = rng.standard_normal((T, H, d_nope))
     q_pe = oracle.widen(w.q_pe)
-    # absorbed query: q_nope @ W_UK, kv_lora_rank wide
-    q_abs = np.einsum("thd,hdr->thr", q_orig, W_UK)
+    # absorbed query: q_nope @ W_UK, kv_lora_rank wide (the oracle's
+    # projections, pinned here by the non-absorbed brute force below)
+    q_abs = oracle.absorb_query(q_orig, W_UK)
     o_lat, lse = oracle.attention(q_abs, q_pe, w.kv_cache, w.qo_indptr, w.kv_indptr,
                                   w.kv_indices, w.kv_last_page_len, page_size, causal, SM)
-    o_abs = np.einsum("thr,hrv->thv", o_lat, W_UV)
+    o_abs = oracle.up_project(o_lat, W_UV)
 
     sm = float(np.float32(SM))
     for b in range(w.batch):
@@ -380,3 +381,33 @@ def test_golden_tiny_fixture():
     o, lse = _run(W.tiny())
     np.testing.assert_allclose(lse, np.array(doc["lse"]), rtol=1e-13, atol=1e-13)
     np.testing.assert_allclose(o[:, :, doc["cols"]], np.array(doc["o_cols"]), rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# The projections on their own: closed forms and loops.
+# ---------------------------------------------------------------------------
+
+def test_projection_closed_forms_and_loops():
+    rng = np.random.default_rng(3)
+    T, H = 5, 3
+    q = W.f32_to_bf16_bits(rng.standard_normal((T, H, 128), dtype=np.float32))
+    # W_UK[h] = [I_128 | 0] (head 0), a column permutation (head 1), 2 I (head 2)
+    w = np.zeros((H, 128, 512))
+    w[0, :, :128] = np.eye(128)
+    perm = rng.permutation(512)[:128]
+    w[1, np.arange(128), perm] = 1.0
+    w[2, :, 256:384] = 2.0 * np.eye(128)
+    out = oracle.absorb_query(q, w)
+    qf = oracle.widen(q)
+    assert np.array_equal(out[:, 0, :128], qf[:, 0]) and not out[:, 0, 128:].any()
+    assert np.array_equal(out[:, 1, perm], qf[:, 1])
+    assert np.array_equal(out[:, 2, 256:384], 2.0 * qf[:, 2])
+    # up-projection by explicit loops
+    o = rng.standard_normal((2, 2, 512))
+    wv = rng.standard_normal((2, 512, 128))
+    ref = np.zeros((2, 2, 128))
+    for t in range(2):
+        for h in range(2):
+            for n in range(128):
+                ref[t, h, n] = sum(o[t, h, k] * wv[h, k, n] for k in range(512))
+    np.testing.assert_allclose(oracle.up_project(o, wv), ref, rtol=1e-12, atol=1e-12)
