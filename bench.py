@@ -23,6 +23,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -124,6 +125,10 @@ def run_steps(w, steps, warmup, copies=3):
         step(k)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # Python's cyclic collector would pause the host loop for tens of ms
+    # (with torch loaded) somewhere inside the timed steps.
+    gc.collect()
+    gc.disable()
     t0 = time.perf_counter()
     e0.record()
     for k in range(steps):
@@ -131,6 +136,7 @@ def run_steps(w, steps, warmup, copies=3):
     e1.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
+    gc.enable()
     run_ms = e0.elapsed_time(e1) / steps
     stats = plan.stats()
     plan.close()
@@ -194,7 +200,42 @@ def other_workloads(steps):
     print("[bench] mixed batch, extra segment and merge done", file=sys.stderr, flush=True)
     out["append_kv"] = [append_kv_entry(W.decode_batch()), append_kv_entry(W.chunked_prefill())]
     print("[bench] KV append done", file=sys.stderr, flush=True)
+    out["projections"] = [projection_entry(kind, T) for kind in ("absorb", "up_project")
+                          for T in (64, 4096)]
+    print("[bench] projections done", file=sys.stderr, flush=True)
     return out
+
+
+def projection_entry(kind, T, H=128, n=20):
+    """mla_absorb_query ([T,H,128] x [H,128,512]) or mla_up_project
+    ([T,H,512] x [H,512,128]) with random bf16 operands; bytes = input +
+    weights + output, flops = 2 T H K N."""
+    import torch
+
+    import paged_mla_attention_amd as pm
+    K, N = (128, 512) if kind == "absorb" else (512, 128)
+    x = torch.randn(T, H, K, device="cuda").to(torch.bfloat16)
+    w = (torch.randn(H, K, N, device="cuda") * K ** -0.5).to(torch.bfloat16)
+    out = torch.empty(T, H, N, device="cuda", dtype=torch.bfloat16)
+    fn = pm.absorb_query if kind == "absorb" else pm.up_project
+    for _ in range(3):
+        fn(x, w, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        fn(x, w, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    nbytes = 2 * (T * H * K + H * K * N + T * H * N)
+    flops = 2 * T * H * K * N
+    gbs, tfs = nbytes / (ms * 1e-3) / 1e9, flops / (ms * 1e-3) / 1e12
+    bound = "hbm" if nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) else "mfma"
+    return {"workload": f"{kind} T={T} H={H} K={K} N={N}", "run_ms": round(ms, 4),
+            "GB_s": round(gbs, 1), "TFLOP_s": round(tfs, 1), "bound": bound,
+            "frac": round(gbs / HBM_PEAK_GBS if bound == "hbm" else tfs / MFMA_BF16_PEAK_TFLOPS, 4),
+            "algorithmic_bytes": nbytes, "algorithmic_flops": flops}
 
 
 def append_kv_entry(w, n=20):

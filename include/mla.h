@@ -151,6 +151,26 @@ mla_status mla_run(mla_plan_t plan, const void* q_nope, const void* q_pe,
 mla_status mla_append_kv(mla_plan_t plan, const void* ckv, const void* kpe, void* kv_cache,
                          mla_stream_t stream);
 
+/* The projections either side of the kernel (module description of the
+ * flashinfer_mla page: the query entering the kernel is absorbed,
+ * q_nope @ W_UK, and the latent output is brought back to the value heads by
+ * W_UV), per head h, in bf16 with fp32 accumulation:
+ *   mla_absorb_query: q_abs[t,h,:] = q_nope[t,h,:] @ w_uk[h]
+ *     q_nope bf16 [T, H, 128], w_uk bf16 [H, 128, 512] (row k of head h holds
+ *     the 512 latent weights of nope dim k), q_abs bf16 [T, H, 512];
+ *   mla_up_project: v[t,h,:] = o[t,h,:] @ w_uv[h]
+ *     o bf16 [T, H, 512] (what mla_run writes), w_uv bf16 [H, 512, 128],
+ *     v bf16 [T, H, 128].
+ * (128 = the nope and value head dims; the pages state only the 192-wide
+ * softmax scale, 192 = 128 + 64.)  Device memory, row-major; the output may
+ * not alias the inputs.  Enqueued on `stream`, no allocation or
+ * synchronisation.  MLA_E_INVALID for NULL pointers (with T > 0),
+ * num_tokens < 0 or num_heads outside [1, 65535]. */
+mla_status mla_absorb_query(const void* q_nope, const void* w_uk, void* q_abs, int64_t num_tokens,
+                            int32_t num_heads, mla_stream_t stream);
+mla_status mla_up_project(const void* o, const void* w_uv, void* v, int64_t num_tokens,
+                          int32_t num_heads, mla_stream_t stream);
+
 /* Merge two attention results over disjoint key segments of the same
  * queries through their LSEs (FlashInferMLAManager.run: the LSE is returned
  * for merging with another key segment):

@@ -25,6 +25,7 @@ QK_ROPE_HEAD_DIM = 64
 
 __all__ = [
     "MLAPlan", "mla_plan_create", "mla_plan", "mla_run", "mla_append_kv", "mla_merge_state",
+    "mla_absorb_query", "mla_up_project", "absorb_query", "up_project",
     "mla_plan_destroy", "mla_plan_stats", "merge_state", "schedule", "append_rows", "library",
 ]
 
@@ -224,6 +225,50 @@ class MLAPlan:
             self.close()
         except Exception:
             pass
+
+
+def mla_absorb_query(q_nope: int, w_uk: int, q_abs: int, num_tokens: int, num_heads: int,
+                     stream: int) -> None:
+    lib = library()
+    _native.check(lib, lib.mla_absorb_query(q_nope, w_uk, q_abs, num_tokens, num_heads, stream))
+
+
+def mla_up_project(o: int, w_uv: int, v: int, num_tokens: int, num_heads: int,
+                   stream: int) -> None:
+    lib = library()
+    _native.check(lib, lib.mla_up_project(o, w_uv, v, num_tokens, num_heads, stream))
+
+
+NOPE_HEAD_DIM = 128
+V_HEAD_DIM = 128
+
+
+def absorb_query(q_nope, w_uk, out=None, stream=None):
+    """``q_nope [T, H, 128] @ w_uk [H, 128, 512]`` per head -> ``[T, H, 512]``
+    (bf16 tensors on the GPU)."""
+    import torch
+    T, H = int(q_nope.shape[0]), int(q_nope.shape[1])
+    if out is None:
+        out = torch.empty((T, H, KV_LORA_RANK), dtype=torch.bfloat16, device=q_nope.device)
+    mla_absorb_query(_dev_ptr(q_nope, "q_nope", torch.bfloat16, (T, H, NOPE_HEAD_DIM)),
+                     _dev_ptr(w_uk, "w_uk", torch.bfloat16, (H, NOPE_HEAD_DIM, KV_LORA_RANK)),
+                     _dev_ptr(out, "out", torch.bfloat16, (T, H, KV_LORA_RANK)), T, H,
+                     _stream_handle(stream))
+    return out
+
+
+def up_project(o, w_uv, out=None, stream=None):
+    """``o [T, H, 512] @ w_uv [H, 512, 128]`` per head -> ``[T, H, 128]``
+    (bf16 tensors on the GPU)."""
+    import torch
+    T, H = int(o.shape[0]), int(o.shape[1])
+    if out is None:
+        out = torch.empty((T, H, V_HEAD_DIM), dtype=torch.bfloat16, device=o.device)
+    mla_up_project(_dev_ptr(o, "o", torch.bfloat16, (T, H, KV_LORA_RANK)),
+                   _dev_ptr(w_uv, "w_uv", torch.bfloat16, (H, KV_LORA_RANK, V_HEAD_DIM)),
+                   _dev_ptr(out, "out", torch.bfloat16, (T, H, V_HEAD_DIM)), T, H,
+                   _stream_handle(stream))
+    return out
 
 
 def merge_state(v_a, s_a, v_b, s_b, v_out=None, s_out=None, stream=None):

@@ -21,6 +21,8 @@ SIGNATURES = {
                            c_int64, c_void_p]),
     "mla_run": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "mla_append_kv": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "mla_absorb_query": (c_int32, [c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_void_p]),
+    "mla_up_project": (c_int32, [c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_void_p]),
     "mla_merge_state": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_int64, c_int32, c_void_p]),
     "mla_plan_destroy": (None, [c_void_p]),

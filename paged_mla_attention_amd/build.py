@@ -23,7 +23,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmla.so")
 HOST_LIB = os.path.join(PKG, "libmla_host.so")
 
-HIP_SOURCES = ["planner.cpp", "capi.cpp", "attention.hip", "merge.hip", "append.hip"]
+HIP_SOURCES = ["planner.cpp", "capi.cpp", "attention.hip", "merge.hip", "append.hip",
+               "projection.hip"]
 ARCH = "gfx950"
 
 

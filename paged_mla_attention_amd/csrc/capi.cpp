@@ -453,6 +453,34 @@ mla_status mla_append_kv(mla_plan_t p, const void* ckv, const void* kpe, void* k
   return MLA_OK;
 }
 
+static mla_status projection(hipError_t (*launch)(const uint16_t*, const uint16_t*, uint16_t*,
+                                                   int64_t, int, hipStream_t),
+                             const char* what, const void* x, const void* w, void* out,
+                             int64_t num_tokens, int32_t num_heads, mla_stream_t stream) {
+  mla::clear_last_error();
+  if (num_tokens < 0 || num_heads < 1 || num_heads > 65535)
+    return fail(MLA_E_INVALID, "bad num_tokens / num_heads");
+  if (num_tokens == 0) return MLA_OK;
+  if (!x || !w || !out) return fail(MLA_E_INVALID, "NULL pointer");
+  const hipError_t e = launch(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w),
+                              static_cast<uint16_t*>(out), num_tokens, num_heads,
+                              static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, what);
+  return MLA_OK;
+}
+
+mla_status mla_absorb_query(const void* q_nope, const void* w_uk, void* q_abs, int64_t num_tokens,
+                            int32_t num_heads, mla_stream_t stream) {
+  return projection(mla::launch_absorb_query, "absorb launch", q_nope, w_uk, q_abs, num_tokens,
+                    num_heads, stream);
+}
+
+mla_status mla_up_project(const void* o, const void* w_uv, void* v, int64_t num_tokens,
+                          int32_t num_heads, mla_stream_t stream) {
+  return projection(mla::launch_up_project, "up-projection launch", o, w_uv, v, num_tokens,
+                    num_heads, stream);
+}
+
 mla_status mla_merge_state(const void* v_a, const float* s_a, const void* v_b, const float* s_b,
                            void* v_out, float* s_out, int64_t num_tokens, int32_t num_heads,
                            mla_stream_t stream) {

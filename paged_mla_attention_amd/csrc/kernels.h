@@ -75,6 +75,16 @@ hipError_t launch_split_merge(const SplitMergeArgs& a, hipStream_t stream);
 hipError_t launch_append_kv(const uint16_t* ckv, const uint16_t* kpe, const AppendRows& rows,
                             uint16_t* cache, int64_t num_tokens, hipStream_t stream);
 
+// Per-head projections: out[t, h, :] = x[t, h, :] @ w[h] (bf16, fp32
+// accumulation).  Absorption: [T, H, 128] x [H, 128, 512]; up-projection:
+// [T, H, 512] x [H, 512, 128].
+constexpr int kNopeDim = 128;
+constexpr int kValueDim = 128;
+hipError_t launch_absorb_query(const uint16_t* q, const uint16_t* w_uk, uint16_t* q_abs, int64_t T,
+                               int H, hipStream_t stream);
+hipError_t launch_up_project(const uint16_t* o, const uint16_t* w_uv, uint16_t* v, int64_t T,
+                             int H, hipStream_t stream);
+
 // Two-segment LSE merge (mla_merge_state).
 hipError_t launch_merge_state(const uint16_t* v_a, const float* s_a, const uint16_t* v_b,
                               const float* s_b, uint16_t* v_out, float* s_out,
