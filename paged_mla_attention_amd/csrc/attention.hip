@@ -470,17 +470,34 @@ struct Attn {
   }
 
   __device__ void run() {
-    if (a.merge_src) {  // each workgroup copies its share of the merge list
-      const int per = (a.merge_ints + static_cast<int>(gridDim.x) - 1) / static_cast<int>(gridDim.x);
-      for (int j = threadIdx.x; j < per; j += blockDim.x) {
-        const int i = static_cast<int>(blockIdx.x) * per + j;
-        if (i < a.merge_ints) a.merge_dst[i] = a.merge_src[i];
-      }
-    }
+    // A schedule in the host slot: the first item is read straight from
+    // first_items (no dependent worker_indptr read) and, where it was staged,
+    // its page list goes out to LDS now, with that read still in flight.
+    // The entry reads (first item, worker_indptr pair) go out together as
+    // one lane-parallel load: lanes 0..7 the item's fields, lanes 8 and 9
+    // this worker's item range.
+    const bool fast_first = kTileInPage && a.first_items != nullptr;
     const bool queued = a.queue_ctr != nullptr;
-    const_i32_t* widx = (const_i32_t*)(a.worker_indptr);
-    const int w_begin = queued ? 0 : widx[blockIdx.x];
-    const int w_end = queued ? 0 : widx[blockIdx.x + 1];
+    if (fast_first && wave == 0)
+      dma4(a.first_pages + blockIdx.x * kFirstPages + lane, lds_base + kPageOff);
+    int entry = 0;
+    {
+      const int l = opaque(lane);
+      const int* src = nullptr;
+      if (l < 8 && fast_first)
+        src = reinterpret_cast<const int*>(a.first_items) + blockIdx.x * 8 + l;
+      else if ((l == 8 || l == 9) && !queued)
+        src = a.worker_indptr + blockIdx.x + (l - 8);
+      if (src) entry = *src;
+    }
+    const int f_token = __builtin_amdgcn_readlane(entry, 0);
+    const int f_begin = __builtin_amdgcn_readlane(entry, 2);
+    const int f_end = __builtin_amdgcn_readlane(entry, 3);
+    const int f_slot = __builtin_amdgcn_readlane(entry, 4);
+    const int f_base = __builtin_amdgcn_readlane(entry, 5);
+    const int f_pages = __builtin_amdgcn_readlane(entry, 7);  // (pad[1]: the page list is staged)
+    const int w_begin = __builtin_amdgcn_readlane(entry, 8);
+    const int w_end = __builtin_amdgcn_readlane(entry, 9);
     const int H = a.num_heads;
     // Work queues: wave 0's lane 0 pops; the next pop from this XCD's queue
     // is issued at the start of each item and read at the start of the next.
@@ -507,12 +524,22 @@ struct Attn {
       } else if (it >= w_end) {
         break;
       }
-      const_i32_t* item = (const_i32_t*)(a.items) + it * 8;  // WorkItem fields
-      token = item[0];
-      kv_begin = item[2];
-      kv_end = item[3];
-      slot = item[4];
-      page_base = item[5];  // kv_indptr[row]
+      // (the first item of a host-slot schedule was read at entry)
+      const bool pre = fast_first && it == w_begin;
+      if (pre) {
+        token = f_token;
+        kv_begin = f_begin;
+        kv_end = f_end;
+        slot = f_slot;
+        page_base = f_base;
+      } else {
+        const_i32_t* item = (const_i32_t*)(a.items) + it * 8;  // WorkItem fields
+        token = item[0];
+        kv_begin = item[2];
+        kv_end = item[3];
+        slot = item[4];
+        page_base = item[5];  // kv_indptr[row]
+      }
       const int ntiles = (kv_end - kv_begin + kTileKeys - 1) / kTileKeys;
 
       f32x16_t o[NW][kDimBlocks];
@@ -542,7 +569,7 @@ struct Attn {
           const int P = a.page_size;
           first_page = kv_begin / P;
           n_pages = (kv_end - 1) / P - first_page + 1;  // <= kMaxItemTiles
-          stage_pages(n_pages);
+          if (!(pre && f_pages)) stage_pages(n_pages);  // (else DMA'd at entry)
         } else {
 #pragma unroll
           for (int t = 0; t < kIdAhead; ++t)
@@ -678,9 +705,10 @@ struct Attn {
         for (int q = 0; q <= kXcds; ++q)
           __hip_atomic_store(a.queue_ctr + q, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    // Every read of the schedule (items, page lists, merge entries) has been
-    // consumed by every wave: tell the host this workgroup is done with the
-    // slot.
+    // Every read of the schedule (items, page lists) has been consumed by
+    // every wave (a workgroup without items waits here for its entry DMA):
+    // tell the host this workgroup is done with the slot.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
     if (a.done_flags && threadIdx.x == 0)
       __hip_atomic_store(a.done_flags + blockIdx.x, a.run_seq, __ATOMIC_RELAXED,

@@ -91,10 +91,8 @@ struct mla_plan_s {
   int32_t* d_qctr = nullptr;  // queue heads + exit count [kXcds + 1], zero between runs
   int append_checked = 0;  // 0: not yet, 1: no slot collision, -1: rejected
   int32_t run_seq = 0;     // sequence number of the last mla_run
-  // Merge entries of a schedule read from a host slot, copied here by the
-  // attention kernel for the merge kernel.
-  int32_t* d_merges = nullptr;
-  size_t merges_cap = 0;   // int32
+  size_t off_first = 0, off_fpages = 0;  // host-slot schedules, page size a multiple of 32
+  bool first_fast = false;
 
   // Split-KV partials: fp32 raw o [slots, H, 512], then lse [slots, H], then
   // 1/l [slots, H].
@@ -122,7 +120,6 @@ void release(mla_plan_s* p) {
     if (sl.h_stage) (void)hipHostFree(sl.h_stage);
     if (sl.flags) (void)hipHostFree(sl.flags);
   }
-  if (p->d_merges) (void)hipFree(p->d_merges);
   if (p->d_qctr) (void)hipFree(p->d_qctr);
   if (p->d_stage) (void)hipFree(p->d_stage);
   if (p->d_part) (void)hipFree(p->d_part);
@@ -215,7 +212,19 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
   const size_t off_app = off_idx + align_up(n_idx_pad);
   const size_t n_q = (mla::kXcds + 1) * sizeof(int32_t);
   const size_t off_q = off_app + align_up(n_app);
-  const size_t total = off_q + align_up(n_q);
+  // A small schedule is read by the kernels from the host slot; its merge
+  // list then goes to the merge kernel as kernel arguments.
+  const bool direct = s.items.size() <= 2 * static_cast<size_t>(p->num_workers) &&
+                      s.merges.size() <= static_cast<size_t>(mla::kInlineMerges);
+  // Each worker's first item, and its page list (up to kFirstPages pages),
+  // at fixed places: the kernel reads them without a dependent read.
+  const bool first_fast = direct && p->page_size % mla::kTileKeys == 0;
+  const size_t n_first = first_fast ? s.num_workers * sizeof(mla::WorkItem) : 0;
+  const size_t n_fpages =
+      first_fast ? static_cast<size_t>(s.num_workers) * mla::kFirstPages * sizeof(int32_t) : 0;
+  const size_t off_first = off_q + align_up(n_q);
+  const size_t off_fpages = off_first + align_up(n_first);
+  const size_t total = off_fpages + align_up(n_fpages);
 
   // This plan's host slot: the last copy from it and the last run that read
   // it must be done before it is refilled.
@@ -236,13 +245,11 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
     if (e != hipSuccess) return hip_fail(e, "hipHostMalloc");
     sl.cap = total;
   }
-  const bool direct = s.items.size() <= 2 * static_cast<size_t>(p->num_workers);
   // Partials: bf16 output rows [slots, H, 512] then fp32 LSE [slots, H].
   const size_t part_floats =
       static_cast<size_t>(s.num_slots) * p->num_heads * (mla::kLoraRank / 2 + 1);
-  const size_t merge_ints = direct ? s.merges.size() * 4 : 0;
   if ((!direct && total > p->d_stage_cap) || part_floats > p->part_cap ||
-      merge_ints > p->merges_cap || (!direct && !p->d_qctr)) {
+      (!direct && !p->d_qctr)) {
     // Buffers may still be read by enqueued kernels of an earlier plan.
     e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
@@ -259,15 +266,6 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
       if (e != hipSuccess) return hip_fail(e, "hipMalloc(queues)");
       e = hipMemset(p->d_qctr, 0, (mla::kXcds + 1) * sizeof(int32_t));
       if (e != hipSuccess) return hip_fail(e, "hipMemset(queues)");
-    }
-    if (merge_ints > p->merges_cap) {
-      if (p->d_merges) (void)hipFree(p->d_merges);
-  if (p->d_qctr) (void)hipFree(p->d_qctr);
-      p->d_merges = nullptr;
-      p->merges_cap = 0;
-      e = hipMalloc(reinterpret_cast<void**>(&p->d_merges), merge_ints * sizeof(int32_t));
-      if (e != hipSuccess) return hip_fail(e, "hipMalloc(merges)");
-      p->merges_cap = merge_ints;
     }
     if (part_floats > p->part_cap) {
       if (p->d_part) (void)hipFree(p->d_part);
@@ -307,6 +305,29 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
   if (s.batch > 0) std::memcpy(h + off_kvp, kv_indptr, n_kvp);
   if (n_idx) std::memcpy(h + off_idx, kv_indices, n_idx);
   if (n_app) std::memcpy(h + off_app, s.append_rows.data(), n_app);
+  if (first_fast) {
+    auto* fi = reinterpret_cast<mla::WorkItem*>(h + off_first);
+    auto* fp = reinterpret_cast<int32_t*>(h + off_fpages);
+    for (int w = 0; w < s.num_workers; ++w) {
+      int32_t* pages = fp + static_cast<size_t>(w) * mla::kFirstPages;
+      if (s.worker_indptr[w] == s.worker_indptr[w + 1]) {
+        fi[w] = mla::WorkItem{0, 0, 0, 0, -1, 0, {0, 0}};
+        std::memset(pages, 0, mla::kFirstPages * sizeof(int32_t));
+        continue;
+      }
+      mla::WorkItem it = s.items[s.worker_indptr[w]];
+      // The item's pages; entries past its last page repeat it (the kernel
+      // never reads them).  pad[1] = 1: the list is staged.
+      const int32_t first_page = it.kv_end > it.kv_begin ? it.kv_begin / p->page_size : 0;
+      const int32_t n_pages =
+          it.kv_end > it.kv_begin ? (it.kv_end - 1) / p->page_size - first_page + 1 : 0;
+      it.pad[1] = n_pages > 0 && n_pages <= mla::kFirstPages ? 1 : 0;
+      const int32_t* src = kv_indices + it.page_base + first_page;
+      for (int i = 0; i < mla::kFirstPages; ++i)
+        pages[i] = it.pad[1] ? src[i < n_pages ? i : n_pages - 1] : 0;
+      fi[w] = it;
+    }
+  }
   std::memset(h + off_idx + n_idx, 0, n_idx_pad - n_idx);
   if (!direct) {
     // (Stream order keeps the copy behind the runs that read the device
@@ -327,6 +348,9 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
   p->off_append = off_app;
   p->off_queues = off_q;
   p->queued = queued;
+  p->off_first = off_first;
+  p->off_fpages = off_fpages;
+  p->first_fast = first_fast;
   p->append_checked = 0;
   p->scale_log2 = sm_scale * 1.44269504088896340736f;
   p->sched = std::move(s);
@@ -381,10 +405,9 @@ mla_status mla_run(mla_plan_t p, const void* q_nope, const void* q_pe, const voi
     capturing = cap != hipStreamCaptureStatusNone;
     a.done_flags = sl.flags;
     a.run_seq = ++p->run_seq;
-    if (!s.merges.empty()) {
-      a.merge_src = reinterpret_cast<const int32_t*>(d + p->off_merges);
-      a.merge_dst = p->d_merges;
-      a.merge_ints = static_cast<int32_t>(s.merges.size() * 4);
+    if (p->first_fast) {
+      a.first_items = reinterpret_cast<const mla::WorkItem*>(d + p->off_first);
+      a.first_pages = reinterpret_cast<const int32_t*>(d + p->off_fpages);
     }
   }
   hipError_t e = mla::launch_attention(a, s.num_workers, stream);
@@ -396,8 +419,10 @@ mla_status mla_run(mla_plan_t p, const void* q_nope, const void* q_pe, const voi
     mla::SplitMergeArgs m{};
     m.part_o = a.part_o;
     m.part_lse = a.part_lse;
-    m.merges = p->direct ? reinterpret_cast<const mla::MergeItem*>(p->d_merges)
-                         : reinterpret_cast<const mla::MergeItem*>(d + p->off_merges);
+    if (p->direct)  // (at most kInlineMerges entries, by the choice of direct)
+      std::memcpy(m.inline_merges, s.merges.data(), s.merges.size() * sizeof(mla::MergeItem));
+    else
+      m.merges = reinterpret_cast<const mla::MergeItem*>(d + p->off_merges);
     m.out = a.out;
     m.lse = lse;
     m.num_heads = p->num_heads;

@@ -24,15 +24,16 @@ struct AttnArgs {
   int32_t num_heads;
   int32_t page_size;
   float scale_log2;  // sm_scale * log2(e)
-  // Schedule read from a pinned host slot: the merge entries (merge_ints
-  // int32) are copied to device memory for the merge kernel, and each
-  // workgroup stores run_seq to done_flags[workgroup] once it has read the
-  // slot for the last time (the host waits on these before refilling it).
-  const int32_t* merge_src;
-  int32_t* merge_dst;
-  int32_t merge_ints;
+  // Schedule read from a pinned host slot: each workgroup stores run_seq to
+  // done_flags[workgroup] once it has read the slot for the last time (the
+  // host waits on these before refilling it).  first_items[w] is worker w's
+  // first item (indexed directly, without worker_indptr), and, when its
+  // first_pages flag (the item's last field) is set, its page list is
+  // first_pages[w * kFirstPages ...], copied to LDS at kernel entry.
   int32_t* done_flags;
   int32_t run_seq;
+  const WorkItem* first_items;
+  const int32_t* first_pages;
   // Work queues (large schedules; nullptr: the static per-workgroup lists of
   // worker_indptr).  Queue x serves the workgroups of XCD x (workgroup w runs
   // on XCD w % kXcds) and holds items [queue_begin[x], queue_begin[x + 1]) in
@@ -55,10 +56,17 @@ struct AppendRows {
   int32_t inline_rows[kInlineRows];
 };
 
+// Pages of a worker's first item staged per worker in the host slot.
+constexpr int kFirstPages = 64;
+// Merge entries handed to the merge kernel as kernel arguments (schedules
+// read from the host slot).
+constexpr int kInlineMerges = 192;
+
 struct SplitMergeArgs {
   const uint16_t* part_o;
   const float* part_lse;
-  const MergeItem* merges;
+  const MergeItem* merges;  // nullptr: inline_merges
+  MergeItem inline_merges[kInlineMerges];
   uint16_t* out;
   float* lse;
   int32_t num_heads;

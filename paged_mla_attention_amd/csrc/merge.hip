@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeArgs a) {
   const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (pair >= a.num_merges * H) return;
   const int mi = pair / H, h = pair - mi * H;
-  const MergeItem m = a.merges[mi];
+  const MergeItem m = a.merges ? a.merges[mi] : a.inline_merges[mi];
   const int n = m.num_slots;
   const int64_t base = static_cast<int64_t>(m.first_slot) * H + h;  // slot k: base + k H
   const uint16_t* rows = a.part_o + base * kLoraRank + lane * 8;
