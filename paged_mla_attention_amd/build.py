@@ -67,9 +67,6 @@ def build_library(out: str = LIB, extra=()) -> str:
         _hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         # Keep the compiler from emitting packed fp32 VALU ops.
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        # One lane pops the work queues; the wave-level atomic rewrite would
-        # wait for each pop where it is issued instead of where it is used.
-        "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
         "-I", INCLUDE, "-Wall", "-Wno-unused-function",
         "-Rpass-analysis=kernel-resource-usage",
         *extra, *srcs, "-o", tmp,

@@ -440,35 +440,6 @@ struct Attn {
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   }
 
-  // This XCD's queue is empty: take an item from another queue.  The heads
-  // of all other queues are read at once (one round trip); a queue that
-  // still has items is then popped.  Returns -1 when every queue is empty.
-  // (Wave 0, lane 0 only.)
-  __device__ int steal() const {
-    const int qx = blockIdx.x % kXcds;
-    for (;;) {
-      int head[kXcds - 1];
-#pragma unroll
-      for (int k = 0; k < kXcds - 1; ++k)
-        head[k] = __hip_atomic_load(a.queue_ctr + (qx + 1 + k) % kXcds, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT);
-      // Start the scan at a workgroup-dependent queue, so the workgroups of
-      // one XCD spread over the others.
-      int pick = -1;
-      const int s0 = (blockIdx.x / kXcds) % (kXcds - 1);
-#pragma unroll
-      for (int k = 0; k < kXcds - 1; ++k) {
-        const int kk = (s0 + k) % (kXcds - 1);
-        const int q = (qx + 1 + kk) % kXcds;
-        if (pick < 0 && head[kk] < a.queue_begin[q + 1] - a.queue_begin[q]) pick = q;
-      }
-      if (pick < 0) return -1;
-      const int i = __hip_atomic_fetch_add(a.queue_ctr + pick, 1, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-      if (i < a.queue_begin[pick + 1] - a.queue_begin[pick]) return a.queue_begin[pick] + i;
-    }
-  }
-
   __device__ void run() {
     // A schedule in the host slot: the first item is read straight from
     // first_items (no dependent worker_indptr read) and, where it was staged,
@@ -477,7 +448,6 @@ struct Attn {
     // one lane-parallel load: lanes 0..7 the item's fields, lanes 8 and 9
     // this worker's item range.
     const bool fast_first = kTileInPage && a.first_items != nullptr;
-    const bool queued = a.queue_ctr != nullptr;
     if (fast_first && wave == 0)
       dma4(a.first_pages + blockIdx.x * kFirstPages + lane, lds_base + kPageOff);
     int entry = 0;
@@ -486,7 +456,7 @@ struct Attn {
       const int* src = nullptr;
       if (l < 8 && fast_first)
         src = reinterpret_cast<const int*>(a.first_items) + blockIdx.x * 8 + l;
-      else if ((l == 8 || l == 9) && !queued)
+      else if (l == 8 || l == 9)
         src = a.worker_indptr + blockIdx.x + (l - 8);
       if (src) entry = *src;
     }
@@ -499,31 +469,8 @@ struct Attn {
     const int w_begin = __builtin_amdgcn_readlane(entry, 8);
     const int w_end = __builtin_amdgcn_readlane(entry, 9);
     const int H = a.num_heads;
-    // Work queues: wave 0's lane 0 pops; the next pop from this XCD's queue
-    // is issued at the start of each item and read at the start of the next.
-    const int qx = blockIdx.x % kXcds;
-    int q_raw = 0;
-    if (queued && wave == 0 && lane == 0)
-      q_raw = __hip_atomic_fetch_add(a.queue_ctr + qx, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-    for (int it = w_begin;; ++it) {
-      if (queued) {
-        int* qw = reinterpret_cast<int*>(smem + kFlagOff) + 16;
-        if (wave == 0 && lane == 0) {
-          const int b = a.queue_begin[qx], len = a.queue_begin[qx + 1] - b;
-          const bool own = q_raw < len;
-          const int got = own ? b + q_raw : steal();
-          qw[0] = got;
-          if (own)
-            q_raw = __hip_atomic_fetch_add(a.queue_ctr + qx, 1, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-        }
-        lds_barrier();
-        it = __builtin_amdgcn_readfirstlane(qw[0]);
-        if (it < 0) break;
-      } else if (it >= w_end) {
-        break;
-      }
+    for (int it = w_begin; it < w_end; ++it) {
       // (the first item of a host-slot schedule was read at entry)
       const bool pre = fast_first && it == w_begin;
       if (pre) {
@@ -695,15 +642,6 @@ struct Attn {
         m_ref = fmaxf(m_seen, __shfl_xor(m_seen, 32));  // the head's largest score
       }
       finish(o, m_ref, l_run);
-    }
-    if (queued && wave == 0 && lane == 0) {
-      // Every queue is empty for this workgroup; the last one out resets the
-      // counters for the next run (all other pops have returned by then).
-      const int d = __hip_atomic_fetch_add(a.queue_ctr + kXcds, 1, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-      if (d == static_cast<int>(gridDim.x) - 1)
-        for (int q = 0; q <= kXcds; ++q)
-          __hip_atomic_store(a.queue_ctr + q, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     // Every read of the schedule (items, page lists) has been consumed by
     // every wave (a workgroup without items waits here for its entry DMA):

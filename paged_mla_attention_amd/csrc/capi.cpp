@@ -16,7 +16,6 @@
 
 #include <cmath>
 #include <cstdio>
-#include <algorithm>
 #include <cstring>
 #include <new>
 #include <thread>
@@ -86,9 +85,6 @@ struct mla_plan_s {
   char* d_stage = nullptr;
   size_t d_stage_cap = 0;
   size_t off_items = 0, off_merges = 0, off_kv_indptr = 0, off_kv_indices = 0, off_append = 0;
-  size_t off_queues = 0;
-  bool queued = false;        // the kernel takes items from per-XCD queues
-  int32_t* d_qctr = nullptr;  // queue heads + exit count [kXcds + 1], zero between runs
   int append_checked = 0;  // 0: not yet, 1: no slot collision, -1: rejected
   int32_t run_seq = 0;     // sequence number of the last mla_run
   size_t off_first = 0, off_fpages = 0;  // host-slot schedules, page size a multiple of 32
@@ -120,7 +116,6 @@ void release(mla_plan_s* p) {
     if (sl.h_stage) (void)hipHostFree(sl.h_stage);
     if (sl.flags) (void)hipHostFree(sl.flags);
   }
-  if (p->d_qctr) (void)hipFree(p->d_qctr);
   if (p->d_stage) (void)hipFree(p->d_stage);
   if (p->d_part) (void)hipFree(p->d_part);
   delete p;
@@ -210,8 +205,6 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
   const size_t off_idx = off_kvp + align_up(n_kvp);
   const size_t n_app = s.append_rows.size() * sizeof(int32_t);
   const size_t off_app = off_idx + align_up(n_idx_pad);
-  const size_t n_q = (mla::kXcds + 1) * sizeof(int32_t);
-  const size_t off_q = off_app + align_up(n_app);
   // A small schedule is read by the kernels from the host slot; its merge
   // list then goes to the merge kernel as kernel arguments.
   const bool direct = s.items.size() <= 2 * static_cast<size_t>(p->num_workers) &&
@@ -222,7 +215,7 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
   const size_t n_first = first_fast ? s.num_workers * sizeof(mla::WorkItem) : 0;
   const size_t n_fpages =
       first_fast ? static_cast<size_t>(s.num_workers) * mla::kFirstPages * sizeof(int32_t) : 0;
-  const size_t off_first = off_q + align_up(n_q);
+  const size_t off_first = off_app + align_up(n_app);
   const size_t off_fpages = off_first + align_up(n_first);
   const size_t total = off_fpages + align_up(n_fpages);
 
@@ -248,8 +241,7 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
   // Partials: bf16 output rows [slots, H, 512] then fp32 LSE [slots, H].
   const size_t part_floats =
       static_cast<size_t>(s.num_slots) * p->num_heads * (mla::kLoraRank / 2 + 1);
-  if ((!direct && total > p->d_stage_cap) || part_floats > p->part_cap ||
-      (!direct && !p->d_qctr)) {
+  if ((!direct && total > p->d_stage_cap) || part_floats > p->part_cap) {
     // Buffers may still be read by enqueued kernels of an earlier plan.
     e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
@@ -260,12 +252,6 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
       e = hipMalloc(reinterpret_cast<void**>(&p->d_stage), total);
       if (e != hipSuccess) return hip_fail(e, "hipMalloc(schedule)");
       p->d_stage_cap = total;
-    }
-    if (!direct && !p->d_qctr) {
-      e = hipMalloc(reinterpret_cast<void**>(&p->d_qctr), (mla::kXcds + 1) * sizeof(int32_t));
-      if (e != hipSuccess) return hip_fail(e, "hipMalloc(queues)");
-      e = hipMemset(p->d_qctr, 0, (mla::kXcds + 1) * sizeof(int32_t));
-      if (e != hipSuccess) return hip_fail(e, "hipMemset(queues)");
     }
     if (part_floats > p->part_cap) {
       if (p->d_part) (void)hipFree(p->d_part);
@@ -278,29 +264,8 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
   }
   char* h = sl.h_stage;
   std::memcpy(h, s.worker_indptr.data(), n_wi);
-  // Large schedules go to per-XCD queues: queue x lists the items of the
-  // workgroups x, x + kXcds, x + 2 kXcds, ... (those on XCD x) in that order,
-  // so the workgroups of one XCD share neighbouring tokens' keys as the
-  // static lists do, and run ahead into other queues when theirs is empty.
-  const bool queued = !direct && s.num_workers % mla::kXcds == 0;
-  if (queued) {
-    auto* qi = reinterpret_cast<mla::WorkItem*>(h + off_items);
-    auto* qb = reinterpret_cast<int32_t*>(h + off_q);
-    int32_t n = 0;
-    for (int x = 0; x < mla::kXcds; ++x) {
-      qb[x] = n;
-      for (int w = x; w < s.num_workers; w += mla::kXcds)
-        for (int32_t i = s.worker_indptr[w]; i < s.worker_indptr[w + 1]; ++i) qi[n++] = s.items[i];
-      // Longest items first, so the last ones popped are short and the
-      // workgroups finish together (items of equal length keep their order).
-      std::stable_sort(qi + qb[x], qi + n, [](const mla::WorkItem& u, const mla::WorkItem& v) {
-        return u.kv_end - u.kv_begin > v.kv_end - v.kv_begin;
-      });
-    }
-    qb[mla::kXcds] = n;
-  } else if (n_items) {
-    std::memcpy(h + off_items, s.items.data(), n_items);
-  }
+  if (n_items) std::memcpy(h + off_items, s.items.data(), n_items);
+
   if (n_merges) std::memcpy(h + off_merges, s.merges.data(), n_merges);
   if (s.batch > 0) std::memcpy(h + off_kvp, kv_indptr, n_kvp);
   if (n_idx) std::memcpy(h + off_idx, kv_indices, n_idx);
@@ -346,8 +311,6 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
   p->off_kv_indptr = off_kvp;
   p->off_kv_indices = off_idx;
   p->off_append = off_app;
-  p->off_queues = off_q;
-  p->queued = queued;
   p->off_first = off_first;
   p->off_fpages = off_fpages;
   p->first_fast = first_fast;
@@ -389,10 +352,6 @@ mla_status mla_run(mla_plan_t p, const void* q_nope, const void* q_pe, const voi
   a.num_heads = p->num_heads;
   a.page_size = p->page_size;
   a.scale_log2 = p->scale_log2;
-  if (p->queued) {
-    a.queue_begin = reinterpret_cast<const int32_t*>(d + p->off_queues);
-    a.queue_ctr = p->d_qctr;
-  }
   // A schedule read from the host slot: the attention workgroups report when
   // they are done with it (no event between the kernels; runs of one plan
   // are stream-ordered, so a slot's flags only grow), and the merge list

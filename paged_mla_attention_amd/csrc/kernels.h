@@ -34,18 +34,8 @@ struct AttnArgs {
   int32_t run_seq;
   const WorkItem* first_items;
   const int32_t* first_pages;
-  // Work queues (large schedules; nullptr: the static per-workgroup lists of
-  // worker_indptr).  Queue x serves the workgroups of XCD x (workgroup w runs
-  // on XCD w % kXcds) and holds items [queue_begin[x], queue_begin[x + 1]) in
-  // the planner's order; queue_ctr[x] is its head and queue_ctr[kXcds]
-  // counts the workgroups that found every queue empty.  All are zero
-  // between runs (the last workgroup out resets them).
-  const int32_t* queue_begin;  // [kXcds + 1]
-  int32_t* queue_ctr;          // [kXcds + 1]
 };
 
-// XCDs of the device: workgroups are dispatched to them round-robin.
-constexpr int kXcds = 8;
 
 // The append kernel's destination rows: a device/host array, or, for a few
 // tokens, the values themselves (kernel arguments need no memory read

@@ -1,9 +1,8 @@
-"""mla_run (and mla_append_kv) captured in a HIP graph and replayed: every
-replay, with eager work and synchronisations between the replays, matches
-the eager result bit for bit.  Covers a schedule the kernels read from the
-pinned host slot (decode-sized) and one read from the device copy through
-the per-XCD work queues (prefill-sized), whose counters the kernel itself
-resets for the next replay."""
+"""mla_run captured in a HIP graph and replayed: every replay, with eager
+work and synchronisations between the replays, matches the eager result bit
+for bit.  Covers a schedule the kernels read from the pinned host slot
+(decode-sized, released by the kernels' flags) and one read from the
+device copy (prefill-sized)."""
 
 import numpy as np
 import pytest
