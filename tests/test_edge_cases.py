@@ -1,0 +1,82 @@
+"""Edge cases through the C ABI against the fp64 oracle: rows longer than the
+longest work item (split at the item cap as well as for balance), with tiles
+inside pages and with per-key page ids, batches whose queries see no keys,
+an empty batch, a single head, and many short prefill items per worker."""
+
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_util import assert_close, oracle_of, run_library
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_mla_attention_amd as pm
+    pm.library()
+
+
+@pytest.mark.parametrize("page_size", [64, 1])
+def test_rows_longer_than_an_item(page_size):
+    """100,000 keys (over 3,000 tiles; an item holds at most 1,024) in one
+    decode row next to a short one, 16 heads."""
+    rng = np.random.default_rng(71 + page_size)
+    w = W.make_workload("long_rows", 0, [100_000, 40], [1, 1], 16, page_size, rng=rng)
+    import paged_mla_attention_amd as pm
+    s = pm.schedule(w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_len, page_size,
+                    w.num_pages, 16, 256)
+    lens = s["items"][:, 3] - s["items"][:, 2]
+    assert lens.max() <= 1024 * 32 and len(s["merges"]) >= 1
+    o, lse = run_library(w)
+    o_ref, l_ref = oracle_of(w)
+    assert_close(o, lse, o_ref, l_ref, f"100k keys P={page_size}")
+
+
+def test_no_query_sees_a_key():
+    """Every row is empty or has more causal queries than keys at the front:
+    the outputs are zero and the LSEs -inf exactly where the oracle says."""
+    rng = np.random.default_rng(5)
+    w = W.make_workload("empty_rows", 0, [0, 0, 3], [2, 1, 6], 32, 16, rng=rng)
+    o, lse = run_library(w)
+    o_ref, l_ref = oracle_of(w)
+    assert np.isneginf(l_ref).any()
+    assert_close(o, lse, o_ref, l_ref, "empty rows")
+
+
+def test_empty_batch():
+    import paged_mla_attention_amd as pm
+    plan = pm.MLAPlan(16, 16)
+    plan.plan([0], [0], [], [], num_cache_pages=1)
+    kv = torch.zeros((1, 16, 576), dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((0, 16, 512), dtype=torch.bfloat16, device="cuda")
+    qp = torch.zeros((0, 16, 64), dtype=torch.bfloat16, device="cuda")
+    o, lse = plan.run(q, qp, kv, return_lse=True)
+    torch.cuda.synchronize()
+    assert o.shape == (0, 16, 512) and lse.shape == (0, 16)
+    plan.close()
+
+
+def test_single_head():
+    rng = np.random.default_rng(9)
+    w = W.make_workload("one_head", 0, [130, 7, 64], [1, 4, 64], 1, 32, rng=rng)
+    o, lse = run_library(w)
+    o_ref, l_ref = oracle_of(w)
+    assert_close(o, lse, o_ref, l_ref, "H=1")
+
+
+def test_many_short_prefill_items_one_wave():
+    """600 causal queries over short rows, 24 heads (one wave per
+    workgroup): several items per worker, many of them a single tile."""
+    rng = np.random.default_rng(13)
+    kv = [40, 200, 33, 500, 96]
+    qo = [40, 150, 10, 300, 100]
+    w = W.make_workload("short_prefill", 0, kv, qo, 24, 16, rng=rng)
+    o, lse = run_library(w)
+    o_ref, l_ref = oracle_of(w)
+    assert_close(o, lse, o_ref, l_ref, "short prefill H=24")
