@@ -139,6 +139,19 @@ def run_steps(w, steps, warmup, copies=3):
     gc.enable()
     run_ms = e0.elapsed_time(e1) / steps
     stats = plan.stats()
+    # The batch is the same every step, so the plans above hit the plan's
+    # cache of its last inputs; a full plan's host time is measured apart,
+    # alternating the table with one that differs in a single entry.
+    last2 = last.copy()
+    last2[int(np.argmax(last2))] -= 1
+    full = []
+    for k in range(20):
+        t1 = time.perf_counter()
+        plan.plan(qo, kvp, idx, last2 if k % 2 == 0 else last, causal=w.causal,
+                  sm_scale=w.sm_scale, num_cache_pages=w.num_pages)
+        full.append(time.perf_counter() - t1)
+    torch.cuda.synchronize()
+    stats["full_plan_host_us"] = round(float(np.median(full)) * 1e6, 1)
     plan.close()
     return wall * 1e3, run_ms, stats
 

@@ -105,6 +105,11 @@ mla_status mla_plan_create(mla_plan_t* out, int32_t device, int32_t num_heads,
  * allocate nothing.  mla_run must be called on `stream` (or a stream
  * ordered after it).
  *
+ * A call whose inputs (all four arrays, batch, causal, sm_scale and
+ * num_cache_pages) equal those of the plan's last successful call returns at
+ * once and keeps that schedule (page "mstar.engine.resources.attn.base",
+ * PlanCacheKey: an unchanged plan need not be rebuilt).
+ *
  * Errors: MLA_E_INVALID for a malformed table (indptr[0] != 0, decreasing
  * indptr, last_page_len outside [1, page_size] on a row with pages, page id
  * out of range, batch < 0, non-finite or non-positive sm_scale).  The plan

@@ -19,6 +19,7 @@
 #include <cstring>
 #include <new>
 #include <thread>
+#include <vector>
 
 #include "kernels.h"
 #include "planner.h"
@@ -63,6 +64,16 @@ struct mla_plan_s {
   int num_workers = 0;
 
   bool planned = false;
+  // The last successful plan's inputs (the plan cache key of the page
+  // "mstar.engine.resources.attn.base", PlanCacheKey: an unchanged plan need
+  // not be rebuilt).  An identical mla_plan keeps the schedule, its staging
+  // slot and its device copy as they are.
+  struct Key {
+    int32_t batch = -1, causal = 0;
+    float sm_scale = 0.f;
+    int64_t num_cache_pages = 0;
+    std::vector<int32_t> qo, kvp, idx, last;
+  } key;
   float scale_log2 = 0.f;
   mla::Schedule sched;
 
@@ -98,6 +109,22 @@ struct mla_plan_s {
 };
 
 namespace {
+
+// Whether a plan call repeats the last successful one exactly.
+bool same_key(const mla_plan_s::Key& k, const int32_t* qo, const int32_t* kvp, const int32_t* idx,
+              const int32_t* last, int32_t batch, int32_t causal, float sm_scale,
+              int64_t num_cache_pages) {
+  if (k.batch != batch || k.causal != (causal != 0) || num_cache_pages != k.num_cache_pages ||
+      std::memcmp(&k.sm_scale, &sm_scale, sizeof(float)) != 0)
+    return false;
+  if (batch == 0) return true;
+  if (!qo || !kvp || !last) return false;
+  const auto eq = [](const std::vector<int32_t>& v, const int32_t* a, size_t n) {
+    return v.size() == n && (n == 0 || (a && std::memcmp(v.data(), a, n * sizeof(int32_t)) == 0));
+  };
+  return eq(k.qo, qo, batch + 1) && eq(k.kvp, kvp, batch + 1) && eq(k.last, last, batch) &&
+         kvp[batch] >= 0 && eq(k.idx, idx, static_cast<size_t>(kvp[batch]));
+}
 
 // Waits until every attention workgroup of the run that last read `sl` from
 // the host has stored its sequence number (or a later one).
@@ -177,6 +204,9 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
   if (!(std::isfinite(sm_scale) && sm_scale > 0.f))
     return fail(MLA_E_INVALID, "sm_scale must be finite and positive");
   hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (p->planned && same_key(p->key, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, batch,
+                             causal, sm_scale, num_cache_pages))
+    return MLA_OK;
   mla::PlanArgs args{qo_indptr, kv_indptr, kv_indices, kv_last_page_len, batch, causal != 0,
                      p->page_size, num_cache_pages, p->num_heads, p->num_workers};
   mla::Schedule s;
@@ -318,6 +348,22 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
   p->scale_log2 = sm_scale * 1.44269504088896340736f;
   p->sched = std::move(s);
   p->planned = true;
+  auto& k = p->key;
+  k.batch = batch;
+  k.causal = causal != 0;
+  k.sm_scale = sm_scale;
+  k.num_cache_pages = num_cache_pages;
+  if (batch > 0) {
+    k.qo.assign(qo_indptr, qo_indptr + batch + 1);
+    k.kvp.assign(kv_indptr, kv_indptr + batch + 1);
+    k.last.assign(kv_last_page_len, kv_last_page_len + batch);
+    k.idx.assign(kv_indices, kv_indices + kv_indptr[batch]);
+  } else {
+    k.qo.clear();
+    k.kvp.clear();
+    k.last.clear();
+    k.idx.clear();
+  }
   return MLA_OK;
 }
 

@@ -286,3 +286,25 @@ def test_error_paths():
     # a failed plan leaves the handle unplanned
     assert lib.mla_run(h, 1, 1, 1, 1, None, None) == 3
     lib.mla_plan_destroy(h)
+
+
+def test_identical_replan_is_kept_and_a_change_is_not():
+    """An identical re-plan keeps the schedule (same output, bit for bit); a
+    table that differs in one entry is planned afresh (matches the oracle for
+    the new table)."""
+    import paged_mla_attention_amd as pm
+    rng = np.random.default_rng(31)
+    w = W.make_workload("replan", 0, [300, 70, 1000], [1, 1, 1], 64, 16, rng=rng)
+    plan = pm.MLAPlan(64, 16)
+    o1, l1 = run_library(w, plan=plan)
+    o2, l2 = run_library(w, plan=plan)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    # shorten the second row by three keys (a different last_page_len)
+    w.kv_last_page_len = w.kv_last_page_len.copy()
+    w.kv_last_page_len[1] -= 3
+    assert w.kv_last_page_len[1] >= 1
+    o3, l3 = run_library(w, plan=plan)
+    o_ref, l_ref = oracle_of(w)
+    assert_close(o3, l3, o_ref, l_ref, "re-planned table")
+    assert not np.array_equal(o3[1], o1[1])
+    plan.close()
