@@ -119,6 +119,21 @@ mla_status mla_plan(mla_plan_t plan, const int32_t* qo_indptr, const int32_t* kv
                     int32_t batch, int32_t causal, float sm_scale,
                     int64_t num_cache_pages, mla_stream_t stream);
 
+/* Reserve fixed capacity (page "mstar.engine.resources.attn.base":
+ * captured_page_capacity and static buffers, so a captured graph stays valid
+ * while the batch changes): later plans of at most max_batch rows,
+ * max_tokens query tokens and max_kv_indices page ids are laid out at fixed
+ * places of the plan's device buffer, copied there on the plan's stream, and
+ * every value the kernels need (scale, merge count) is read from that
+ * buffer.  An mla_run captured once then runs whatever batch was planned
+ * last (q, out and lse must be sized for max_tokens; rows beyond the batch's
+ * tokens are untouched; capture after a plan with at least one token).  A
+ * plan beyond the capacity fails with MLA_E_INVALID and keeps the previous
+ * one.  Synchronises the device and allocates; call it before capturing.
+ * After it the plan must be planned again. */
+mla_status mla_plan_reserve(mla_plan_t plan, int32_t max_batch, int64_t max_tokens,
+                            int64_t max_kv_indices);
+
 /* Run the planned batch (FlashInferMLAWrapper.run): all pointers are device
  * memory with the layouts above; `lse` may be NULL when not wanted.  The call
  * only enqueues kernels on `stream` (no allocation, no synchronisation), so

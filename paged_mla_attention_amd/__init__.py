@@ -161,6 +161,15 @@ class MLAPlan:
                                   self.page_size)
         self._planned = None
 
+    def reserve(self, max_batch: int, max_tokens: int, max_kv_indices: int) -> None:
+        """Fix the plan's capacity so that a captured ``run`` stays valid while
+        later ``plan`` calls change the batch (see mla_plan_reserve)."""
+        lib = library()
+        _native.check(lib, lib.mla_plan_reserve(self._h, int(max_batch), int(max_tokens),
+                                                int(max_kv_indices)))
+        self._planned = None
+        self._reserved_tokens = int(max_tokens)
+
     def plan(self, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, causal: bool = True,
              sm_scale: float = 192.0 ** -0.5, num_cache_pages: Optional[int] = None,
              stream=None) -> None:
@@ -178,6 +187,8 @@ class MLAPlan:
             raise RuntimeError("run() before plan()")
         T, pages = self._planned
         H = self.num_heads
+        if getattr(self, "_reserved_tokens", None):
+            T = self._reserved_tokens  # tensors sized for the reserved capacity
         if kv_cache.dim() != 3 or kv_cache.shape[0] < pages:
             raise ValueError(f"kv_cache must be [>= {pages}, page_size, 576]")
         qn = _dev_ptr(q_nope, "q_nope", torch.bfloat16, (T, H, KV_LORA_RANK))

@@ -17,6 +17,7 @@ _f32p = POINTER(c_float)
 # Every function include/mla.h declares, with (restype, argtypes).
 SIGNATURES = {
     "mla_plan_create": (c_int32, [POINTER(c_void_p), c_int32, c_int32, c_int32, c_int32, c_int32]),
+    "mla_plan_reserve": (c_int32, [c_void_p, c_int32, c_int64, c_int64]),
     "mla_plan": (c_int32, [c_void_p, _i32p, _i32p, _i32p, _i32p, c_int32, c_int32, c_float,
                            c_int64, c_void_p]),
     "mla_run": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),

@@ -183,12 +183,14 @@ struct Attn {
   bool head_ok;
   int ld_key, ld_off, qk_off_e, qk_off_o, pv_off0, pv_off1;  // per-lane LDS / row offsets
   uint32_t lds_base;                               // LDS address of the stages
+  float scale_log2;                                // sm_scale * log2(e)
   // current item
   int token, kv_begin, kv_end, slot;
   int page_base;   // index of the row's first page in kv_indices
   int first_page;  // row page index of the item's first key
 
   __device__ Attn(const AttnArgs& args, char* s) : a(args), smem(s) {
+    scale_log2 = args.scale_log2_ptr ? *args.scale_log2_ptr : args.scale_log2;
     const int tid = threadIdx.x;
     lane = tid & 63;
     l32 = lane & 31;
@@ -725,7 +727,7 @@ struct Attn {
     float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < 16; ++j) mx = fmaxf(mx, x[j]);
-    mx *= a.scale_log2;
+    mx *= scale_log2;
     m_seen = fmaxf(m_seen, mx);
     return mx;
   }
@@ -740,7 +742,7 @@ struct Attn {
                                               bf16x8_t (&p)[2]) const {
 #pragma unroll
     for (int j = j0; j < j1; ++j) {
-      const float v = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], a.scale_log2, neg_ref));
+      const float v = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], scale_log2, neg_ref));
       l_run += v;
       p[j >> 3][j & 7] = static_cast<__bf16>(v);
     }

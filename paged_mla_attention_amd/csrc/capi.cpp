@@ -14,6 +14,7 @@
 // that read it.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -95,9 +96,17 @@ struct mla_plan_s {
   bool direct = false;      // the kernels read the schedule from the host slot
   char* d_stage = nullptr;
   size_t d_stage_cap = 0;
-  size_t off_items = 0, off_merges = 0, off_kv_indptr = 0, off_kv_indices = 0, off_append = 0;
+  size_t off_wi = 0, off_items = 0, off_merges = 0, off_kv_indptr = 0, off_kv_indices = 0,
+         off_append = 0;
   int append_checked = 0;  // 0: not yet, 1: no slot collision, -1: rejected
   int32_t run_seq = 0;     // sequence number of the last mla_run
+  // Reserved capacity (mla_plan_reserve): every section at a fixed offset of
+  // the device buffer, the per-plan scalars in a header (scale_log2,
+  // num_merges), so kernels captured once read whatever batch was planned
+  // last.
+  bool reserved = false;
+  int32_t cap_batch = 0;
+  int64_t cap_tokens = 0, cap_nnz = 0, cap_items = 0, cap_merges = 0;
   size_t off_first = 0, off_fpages = 0;  // host-slot schedules, page size a multiple of 32
   bool first_fast = false;
 
@@ -195,6 +204,69 @@ mla_status mla_plan_create(mla_plan_t* out, int32_t device, int32_t num_heads,
   return MLA_OK;
 }
 
+mla_status mla_plan_reserve(mla_plan_t p, int32_t max_batch, int64_t max_tokens,
+                            int64_t max_kv_indices) {
+  mla::clear_last_error();
+  if (!p) return fail(MLA_E_INVALID, "NULL plan");
+  if (max_batch < 1 || max_tokens < 1 || max_kv_indices < 0)
+    return fail(MLA_E_INVALID, "reserved sizes must be positive");
+  DeviceGuard g(p->device);
+  if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
+  const int64_t W = p->num_workers;
+  // Items: one per token, at most two more per worker where the balance cuts
+  // a token, and the cuts of rows longer than the longest item.
+  const int64_t max_keys = max_kv_indices * p->page_size;
+  const int64_t cap_items =
+      max_tokens + 2 * W + max_keys / (int64_t(mla::kTileKeys) * mla::kMaxItemTiles) + 8;
+  const int64_t cap_merges = std::min<int64_t>(max_tokens, cap_items);
+  const size_t total =
+      kAlign + align_up((W + 1) * sizeof(int32_t)) + align_up(cap_items * sizeof(mla::WorkItem)) +
+      align_up(cap_merges * sizeof(mla::MergeItem)) + align_up((max_batch + 1) * sizeof(int32_t)) +
+      align_up((max_kv_indices + mla::kTileKeys) * sizeof(int32_t)) +
+      align_up(max_tokens * sizeof(int32_t));
+  const size_t part_floats = static_cast<size_t>(cap_items) * p->num_heads * (mla::kLoraRank / 2 + 1);
+  // Nothing of an earlier plan may still run while the buffers change.
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+  for (auto& sl : p->slot) {
+    if (sl.wait_seq > 0) wait_flags(p, sl);
+    sl.pending = false;
+    if (total > sl.cap) {
+      if (sl.h_stage) (void)hipHostFree(sl.h_stage);
+      sl.h_stage = nullptr;
+      sl.cap = 0;
+      e = hipHostMalloc(reinterpret_cast<void**>(&sl.h_stage), total, hipHostMallocDefault);
+      if (e != hipSuccess) return hip_fail(e, "hipHostMalloc");
+      sl.cap = total;
+    }
+  }
+  if (total > p->d_stage_cap) {
+    if (p->d_stage) (void)hipFree(p->d_stage);
+    p->d_stage = nullptr;
+    p->d_stage_cap = 0;
+    e = hipMalloc(reinterpret_cast<void**>(&p->d_stage), total);
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(schedule)");
+    p->d_stage_cap = total;
+  }
+  if (part_floats > p->part_cap) {
+    if (p->d_part) (void)hipFree(p->d_part);
+    p->d_part = nullptr;
+    p->part_cap = 0;
+    e = hipMalloc(reinterpret_cast<void**>(&p->d_part), part_floats * sizeof(float));
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(partials)");
+    p->part_cap = part_floats;
+  }
+  p->reserved = true;
+  p->cap_batch = max_batch;
+  p->cap_tokens = max_tokens;
+  p->cap_nnz = max_kv_indices;
+  p->cap_items = cap_items;
+  p->cap_merges = cap_merges;
+  p->planned = false;  // plan again into the reserved layout
+  p->key = mla_plan_s::Key{};
+  return MLA_OK;
+}
+
 mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_indptr,
                     const int32_t* kv_indices, const int32_t* kv_last_page_len, int32_t batch,
                     int32_t causal, float sm_scale, int64_t num_cache_pages,
@@ -229,15 +301,30 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
   // 32-key tile as one scalar block that may run past a row's last page.
   const size_t n_idx = static_cast<size_t>(s.nnz) * sizeof(int32_t);
   const size_t n_idx_pad = n_idx + mla::kTileKeys * sizeof(int32_t);
-  const size_t off_items = align_up(n_wi);
-  const size_t off_merges = off_items + align_up(n_items);
-  const size_t off_kvp = off_merges + align_up(n_merges);
-  const size_t off_idx = off_kvp + align_up(n_kvp);
   const size_t n_app = s.append_rows.size() * sizeof(int32_t);
-  const size_t off_app = off_idx + align_up(n_idx_pad);
+  if (p->reserved &&
+      (s.batch > p->cap_batch || s.num_tokens > p->cap_tokens || s.nnz > p->cap_nnz ||
+       static_cast<int64_t>(s.items.size()) > p->cap_items ||
+       static_cast<int64_t>(s.merges.size()) > p->cap_merges || s.num_slots > p->cap_items))
+    return fail(MLA_E_INVALID, "batch exceeds the plan's reserved capacity");
+  // Section sizes: the schedule's own, or the reserved maxima.
+  const size_t z_wi = n_wi;
+  const size_t z_items = p->reserved ? p->cap_items * sizeof(mla::WorkItem) : n_items;
+  const size_t z_merges = p->reserved ? p->cap_merges * sizeof(mla::MergeItem) : n_merges;
+  const size_t z_kvp = p->reserved ? (p->cap_batch + 1) * sizeof(int32_t) : n_kvp;
+  const size_t z_idx = p->reserved ? (p->cap_nnz + mla::kTileKeys) * sizeof(int32_t) : n_idx_pad;
+  const size_t z_app = p->reserved ? p->cap_tokens * sizeof(int32_t) : n_app;
+  const size_t off_hdr = 0;  // reserved plans: float scale_log2, int32 num_merges
+  const size_t off_wi = p->reserved ? kAlign : 0;
+  const size_t off_items = off_wi + align_up(z_wi);
+  const size_t off_merges = off_items + align_up(z_items);
+  const size_t off_kvp = off_merges + align_up(z_merges);
+  const size_t off_idx = off_kvp + align_up(z_kvp);
+  const size_t off_app = off_idx + align_up(z_idx);
   // A small schedule is read by the kernels from the host slot; its merge
   // list then goes to the merge kernel as kernel arguments.
-  const bool direct = s.items.size() <= 2 * static_cast<size_t>(p->num_workers) &&
+  const bool direct = !p->reserved &&
+                      s.items.size() <= 2 * static_cast<size_t>(p->num_workers) &&
                       s.merges.size() <= static_cast<size_t>(mla::kInlineMerges);
   // Each worker's first item, and its page list (up to kFirstPages pages),
   // at fixed places: the kernel reads them without a dependent read.
@@ -245,7 +332,7 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
   const size_t n_first = first_fast ? s.num_workers * sizeof(mla::WorkItem) : 0;
   const size_t n_fpages =
       first_fast ? static_cast<size_t>(s.num_workers) * mla::kFirstPages * sizeof(int32_t) : 0;
-  const size_t off_first = off_app + align_up(n_app);
+  const size_t off_first = off_app + align_up(z_app);
   const size_t off_fpages = off_first + align_up(n_first);
   const size_t total = off_fpages + align_up(n_fpages);
 
@@ -293,7 +380,13 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
     }
   }
   char* h = sl.h_stage;
-  std::memcpy(h, s.worker_indptr.data(), n_wi);
+  if (p->reserved) {
+    const float sl2 = sm_scale * 1.44269504088896340736f;
+    const int32_t nm = static_cast<int32_t>(s.merges.size());
+    std::memcpy(h + off_hdr, &sl2, sizeof(float));
+    std::memcpy(h + off_hdr + sizeof(float), &nm, sizeof(int32_t));
+  }
+  std::memcpy(h + off_wi, s.worker_indptr.data(), n_wi);
   if (n_items) std::memcpy(h + off_items, s.items.data(), n_items);
 
   if (n_merges) std::memcpy(h + off_merges, s.merges.data(), n_merges);
@@ -336,6 +429,7 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
   p->cur = si;
   p->direct = direct;
 
+  p->off_wi = off_wi;
   p->off_items = off_items;
   p->off_merges = off_merges;
   p->off_kv_indptr = off_kvp;
@@ -380,7 +474,9 @@ mla_status mla_run(mla_plan_t p, const void* q_nope, const void* q_pe, const voi
   if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
   hipStream_t stream = static_cast<hipStream_t>(stream_);
 
-  const size_t slots_h = static_cast<size_t>(s.num_slots) * p->num_heads;
+  // (a reserved plan keeps the LSE section at the reserved offset)
+  const size_t slots_h =
+      static_cast<size_t>(p->reserved ? p->cap_items : s.num_slots) * p->num_heads;
   mla::AttnArgs a{};
   a.q_nope = static_cast<const uint16_t*>(q_nope);
   a.q_pe = static_cast<const uint16_t*>(q_pe);
@@ -391,7 +487,8 @@ mla_status mla_run(mla_plan_t p, const void* q_nope, const void* q_pe, const voi
   a.part_lse = p->d_part ? p->d_part + slots_h * (mla::kLoraRank / 2) : nullptr;
   auto& sl = p->slot[p->cur];
   const char* d = p->direct ? sl.h_stage : p->d_stage;
-  a.worker_indptr = reinterpret_cast<const int32_t*>(d);
+  a.worker_indptr = reinterpret_cast<const int32_t*>(d + p->off_wi);
+  if (p->reserved) a.scale_log2_ptr = reinterpret_cast<const float*>(d);
   a.items = reinterpret_cast<const mla::WorkItem*>(d + p->off_items);
   a.kv_indptr = reinterpret_cast<const int32_t*>(d + p->off_kv_indptr);
   a.kv_indices = reinterpret_cast<const int32_t*>(d + p->off_kv_indices);
@@ -420,7 +517,7 @@ mla_status mla_run(mla_plan_t p, const void* q_nope, const void* q_pe, const voi
   // (Under stream capture a replay reads the slot whenever it runs: the
   // caller must not re-plan twice while such a graph may still replay.)
   if (p->direct && !capturing) sl.wait_seq = a.run_seq;
-  if (!s.merges.empty()) {
+  if (!s.merges.empty() || p->reserved) {
     mla::SplitMergeArgs m{};
     m.part_o = a.part_o;
     m.part_lse = a.part_lse;
@@ -432,6 +529,10 @@ mla_status mla_run(mla_plan_t p, const void* q_nope, const void* q_pe, const voi
     m.lse = lse;
     m.num_heads = p->num_heads;
     m.num_merges = static_cast<int32_t>(s.merges.size());
+    if (p->reserved) {  // (captured kernels cover the reserved count)
+      m.num_merges = static_cast<int32_t>(p->cap_merges);
+      m.num_merges_ptr = reinterpret_cast<const int32_t*>(d + sizeof(float));
+    }
     e = mla::launch_split_merge(m, stream);
     if (e != hipSuccess) return hip_fail(e, "split-merge launch");
   }

@@ -24,6 +24,7 @@ struct AttnArgs {
   int32_t num_heads;
   int32_t page_size;
   float scale_log2;  // sm_scale * log2(e)
+  const float* scale_log2_ptr;  // non-null: read the scale here (reserved plans)
   // Schedule read from a pinned host slot: each workgroup stores run_seq to
   // done_flags[workgroup] once it has read the slot for the last time (the
   // host waits on these before refilling it).  first_items[w] is worker w's
@@ -60,7 +61,8 @@ struct SplitMergeArgs {
   uint16_t* out;
   float* lse;
   int32_t num_heads;
-  int32_t num_merges;
+  int32_t num_merges;             // entries (the grid covers this many)
+  const int32_t* num_merges_ptr;  // non-null: the live count, <= num_merges (reserved plans)
 };
 
 // Attention over every planned work item: one workgroup per worker.

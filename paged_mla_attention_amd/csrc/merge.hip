@@ -35,7 +35,8 @@ __global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeArgs a) {
   const int lane = threadIdx.x & 63;
   const int H = a.num_heads;
   const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (pair >= a.num_merges * H) return;
+  const int num_merges = a.num_merges_ptr ? *a.num_merges_ptr : a.num_merges;
+  if (pair >= num_merges * H) return;
   const int mi = pair / H, h = pair - mi * H;
   const MergeItem m = a.merges ? a.merges[mi] : a.inline_merges[mi];
   const int n = m.num_slots;

@@ -63,3 +63,66 @@ def test_graph_replays_match_eager(shape):
         assert torch.equal(out, ref_o)
     plan.close()
     assert stats["num_workers"] > 0
+
+
+def test_reserved_plan_graph_survives_replans():
+    """A plan with reserved capacity: mla_run captured once, then replayed
+    after plans of three different batches (decode, prefill and mixed rows,
+    different lengths and token counts), each replay matching the oracle for
+    the batch planned last."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_mla_attention_amd as pm
+    import oracle
+    from gpu_util import assert_close
+    H, P = 64, 16
+    batches = [
+        W.make_workload("r1", 0, [300, 70, 1000], [1, 1, 1], H, P, rng=np.random.default_rng(1)),
+        W.make_workload("r2", 0, [2000, 50], [16, 50], H, P, rng=np.random.default_rng(2)),
+        W.make_workload("r3", 0, [40, 900, 123, 777], [5, 1, 1, 30], H, P,
+                        rng=np.random.default_rng(3)),
+    ]
+    max_t, max_pages = 96, max(w.num_pages for w in batches)
+    max_nnz = max(int(w.kv_indptr[-1]) for w in batches)
+    q_pool = torch.zeros((max_t, H, 512), dtype=torch.bfloat16, device="cuda")
+    qp_pool = torch.zeros((max_t, H, 64), dtype=torch.bfloat16, device="cuda")
+    kv_pool = torch.zeros((max_pages, P, 576), dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros((max_t, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros((max_t, H), dtype=torch.float32, device="cuda")
+    plan = pm.MLAPlan(H, P)
+    plan.reserve(8, max_t, max_nnz)
+
+    def load(w):
+        T = w.num_tokens
+        q_pool[:T].copy_(_dev(w.q_nope))
+        qp_pool[:T].copy_(_dev(w.q_pe))
+        kv_pool[:w.num_pages].copy_(_dev(w.kv_cache))
+        plan.plan(w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_len, causal=True,
+                  sm_scale=w.sm_scale, num_cache_pages=max_pages)
+
+    load(batches[0])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        plan.run(q_pool, qp_pool, kv_pool, out=out, lse=lse, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        plan.run(q_pool, qp_pool, kv_pool, out=out, lse=lse)
+    torch.cuda.synchronize()
+    for w in batches + [batches[0]]:
+        load(w)
+        out.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        T = w.num_tokens
+        o = out[:T].view(torch.int16).cpu().numpy().view(np.uint16)
+        o_ref, l_ref = oracle.attention(w.q_nope, w.q_pe, w.kv_cache, w.qo_indptr, w.kv_indptr,
+                                        w.kv_indices, w.kv_last_page_len, P, True, w.sm_scale)
+        assert_close(o, lse[:T].cpu().numpy(), o_ref, l_ref, f"replay after planning {w.name}")
+    with pytest.raises(Exception):  # beyond the reserved capacity
+        big = W.make_workload("big", 0, [100] * 9, [1] * 9, H, P, rng=np.random.default_rng(4))
+        plan.plan(big.qo_indptr, big.kv_indptr, big.kv_indices, big.kv_last_page_len,
+                  num_cache_pages=big.num_pages)
+    plan.close()
