@@ -141,13 +141,15 @@ def run_steps(w, steps, warmup, copies=3):
     stats = plan.stats()
     # The batch is the same every step, so the plans above hit the plan's
     # cache of its last inputs; a full plan's host time is measured apart,
-    # alternating the table with one that differs in a single entry.
-    last2 = last.copy()
-    last2[int(np.argmax(last2))] -= 1
+    # alternating the table with one whose first two page ids are swapped
+    # (valid for any table).
+    idx2 = idx.copy()
+    if idx2.size >= 2:
+        idx2[[0, 1]] = idx2[[1, 0]]
     full = []
     for k in range(20):
         t1 = time.perf_counter()
-        plan.plan(qo, kvp, idx, last2 if k % 2 == 0 else last, causal=w.causal,
+        plan.plan(qo, kvp, idx2 if k % 2 == 0 else idx, last, causal=w.causal,
                   sm_scale=w.sm_scale, num_cache_pages=w.num_pages)
         full.append(time.perf_counter() - t1)
     torch.cuda.synchronize()
