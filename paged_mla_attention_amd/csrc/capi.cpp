@@ -9,9 +9,10 @@
 // host slots.  A small schedule (at most two items per worker, as in
 // decode) is read by the kernels straight from its pinned slot, which saves
 // the upload that would otherwise sit between two steps' kernels; a larger
-// one is copied to the device buffer on the plan's stream.  Before
-// refilling a slot, a plan waits for the last copy from it and the last run
-// that read it.
+// one, and every schedule of a plan with reserved capacity, is copied to
+// the device buffer on the plan's stream.  Before refilling a slot, a plan
+// waits for the last copy from it (an event) and the last run that read it
+// (flags the attention workgroups store).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -78,9 +79,10 @@ struct mla_plan_s {
   float scale_log2 = 0.f;
   mla::Schedule sched;
 
-  // Pinned host staging slots and the device mirror: worker_indptr | items
-  // | merges | kv_indptr | kv_indices | append rows, each section 256-byte
-  // aligned.
+  // Pinned host staging slots and the device mirror: [reserved-plan header]
+  // | worker_indptr | items | merges | kv_indptr | kv_indices | append rows
+  // | [first items | first page lists, for host-slot schedules], each
+  // section 256-byte aligned.
   struct HostSlot {
     char* h_stage = nullptr;
     size_t cap = 0;
@@ -110,10 +112,10 @@ struct mla_plan_s {
   size_t off_first = 0, off_fpages = 0;  // host-slot schedules, page size a multiple of 32
   bool first_fast = false;
 
-  // Split-KV partials: fp32 raw o [slots, H, 512], then lse [slots, H], then
-  // 1/l [slots, H].
+  // Split-KV partials: bf16 o [slots, H, 512] (normalised by the piece's own
+  // denominator), then fp32 lse [slots, H].
   float* d_part = nullptr;
-  size_t part_cap = 0;  // floats
+  size_t part_cap = 0;  // 4-byte words
 
 };
 
@@ -297,8 +299,8 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
   const size_t n_items = s.items.size() * sizeof(mla::WorkItem);
   const size_t n_merges = s.merges.size() * sizeof(mla::MergeItem);
   const size_t n_kvp = static_cast<size_t>(s.batch + 1) * sizeof(int32_t);
-  // kv_indices plus 32 spare entries: the kernel reads the page ids of a
-  // 32-key tile as one scalar block that may run past a row's last page.
+  // kv_indices plus 32 zeroed spare entries (slack past the last row's
+  // pages).
   const size_t n_idx = static_cast<size_t>(s.nnz) * sizeof(int32_t);
   const size_t n_idx_pad = n_idx + mla::kTileKeys * sizeof(int32_t);
   const size_t n_app = s.append_rows.size() * sizeof(int32_t);
@@ -388,7 +390,6 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
   }
   std::memcpy(h + off_wi, s.worker_indptr.data(), n_wi);
   if (n_items) std::memcpy(h + off_items, s.items.data(), n_items);
-
   if (n_merges) std::memcpy(h + off_merges, s.merges.data(), n_merges);
   if (s.batch > 0) std::memcpy(h + off_kvp, kv_indptr, n_kvp);
   if (n_idx) std::memcpy(h + off_idx, kv_indices, n_idx);
