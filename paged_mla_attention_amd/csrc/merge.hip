@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeArgs a) {
 #pragma unroll
   for (int b = 0; b < kBatch; ++b) {
     const int k = b < n ? b : n - 1;  // (a repeated row gets weight 0)
-    r[b] = *reinterpret_cast<const u32x4_t*>(rows + k * row_step);
+    r[b] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(rows + k * row_step));
   }
   const float s_lane = lane < n ? a.part_lse[base + static_cast<int64_t>(lane) * H] : -INFINITY;
   float M = s_lane;
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeArgs a) {
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
           const int k = k0 + b < n ? k0 + b : n - 1;
-          r[b] = *reinterpret_cast<const u32x4_t*>(rows + k * row_step);
+          r[b] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(rows + k * row_step));
         }
       }
 #pragma unroll
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeArgs a) {
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     o[j] = to_bf16(acc[2 * j] * inv) | (static_cast<unsigned>(to_bf16(acc[2 * j + 1] * inv)) << 16);
-  *reinterpret_cast<u32x4_t*>(a.out + th * kLoraRank + lane * 8) = o;
+  __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(a.out + th * kLoraRank + lane * 8));
   if (a.lse && lane == 0) a.lse[th] = wsum > 0.f ? M + logf(wsum) : -INFINITY;
 }
 
@@ -106,8 +106,10 @@ __global__ __launch_bounds__(256) void merge_state_kernel(const uint16_t* v_a,
   const float sa = s_a[pair], sb = s_b[pair];
   const float M = fmaxf(sa, sb);
   const int64_t off = pair * kLoraRank + lane * 8;
-  const u32x4_t va = *reinterpret_cast<const u32x4_t*>(v_a + off);
-  const u32x4_t vb = *reinterpret_cast<const u32x4_t*>(v_b + off);
+  // (streamed once: non-temporal loads and store keep them from displacing
+  // other data in the caches)
+  const u32x4_t va = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(v_a + off));
+  const u32x4_t vb = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(v_b + off));
   float wa = 0.f, wb = 0.f;
   if (M != -INFINITY) {
     wa = (sa == -INFINITY) ? 0.f : expf(sa - M);
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(256) void merge_state_kernel(const uint16_t* v_a,
     const float hi = ca * bf16_hi(va[j]) + cb * bf16_hi(vb[j]);
     r[j] = to_bf16(lo) | (static_cast<unsigned>(to_bf16(hi)) << 16);
   }
-  *reinterpret_cast<u32x4_t*>(v_out + off) = r;
+  __builtin_nontemporal_store(r, reinterpret_cast<u32x4_t*>(v_out + off));
   if (lane == 0) s_out[pair] = z > 0.f ? M + logf(z) : -INFINITY;
 }
 
