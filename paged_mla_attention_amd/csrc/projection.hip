@@ -184,7 +184,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void h
       for (int j = 0; j < 8; ++j) {
         const int64_t t = tw + 4 * j + pr;
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(piece + ((4 * j + pr) * kPieceRow + pc) * 2);
-        if (t < T) *reinterpret_cast<u32x4_t*>(out + (t * H + h) * N + n_base + pc) = v;
+        // (whole 16-byte pieces of rows written once: non-temporal)
+        if (t < T)
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(out + (t * H + h) * N + n_base + pc));
       }
       wave_lds_sync();  // (the piece is rewritten next)
     } else if (tw + l32 < T) {
