@@ -504,9 +504,11 @@ struct Attn {
             for (int j = 0; j < 16; ++j) o[g][db][j] = 0.f;
         l_run = 0.f;
         m_seen = -INFINITY;
-        if (ntiles == 0) break;
         // Every wave is done with the previous item's (or attempt's) LDS.
+        // (An item without keys goes straight to its finish, whose 1/l
+        // exchange slots the previous item's finish may still be reading.)
         lds_barrier();
+        if (ntiles == 0) break;
         // This wave's query rows go through LDS: whole rows per DMA, where
         // loading them straight into the MFMA operand layout would touch
         // 32 rows per load (see stage_query).  The page ids go out in the

@@ -23,6 +23,7 @@
 #include <thread>
 #include <vector>
 
+#include "host_wait.h"
 #include "kernels.h"
 #include "planner.h"
 
@@ -138,21 +139,32 @@ bool same_key(const mla_plan_s::Key& k, const int32_t* qo, const int32_t* kvp, c
 }
 
 // Waits until every attention workgroup of the run that last read `sl` from
-// the host has stored its sequence number (or a later one).
-void wait_flags(const mla_plan_s* p, mla_plan_s::HostSlot& sl) {
-  const volatile int32_t* f = sl.flags;
-  for (int w = 0; w < p->num_workers; ++w)
-    while (static_cast<int32_t>(f[w] - sl.wait_seq) < 0) std::this_thread::yield();
+// the host has stored its sequence number (or a later one), for at most
+// kSlotWaitTimeoutS.  On time-out the slot stays marked as in use and the
+// call fails with MLA_E_HIP.
+mla_status wait_flags(const mla_plan_s* p, mla_plan_s::HostSlot& sl) {
+  int late = -1;
+  if (!mla::wait_for_flags(sl.flags, p->num_workers, sl.wait_seq, mla::kSlotWaitTimeoutS, &late)) {
+    char buf[256];
+    std::snprintf(buf, sizeof buf,
+                  "run %d reading staging slot %d has not finished after %.0f s (workgroup %d)",
+                  static_cast<int>(sl.wait_seq), static_cast<int>(&sl - p->slot), mla::kSlotWaitTimeoutS,
+                  late);
+    mla::set_last_error(buf);
+    return MLA_E_HIP;
+  }
   sl.wait_seq = 0;
+  return MLA_OK;
 }
 
 void release(mla_plan_s* p) {
   for (auto& sl : p->slot) {
     if (sl.pending) (void)hipEventSynchronize(sl.done);
-    if (sl.wait_seq > 0) wait_flags(p, sl);
+    // A slot that a run may still read is leaked rather than freed under it.
+    const bool busy = sl.wait_seq > 0 && wait_flags(p, sl) != MLA_OK;
     if (sl.done) (void)hipEventDestroy(sl.done);
-    if (sl.h_stage) (void)hipHostFree(sl.h_stage);
-    if (sl.flags) (void)hipHostFree(sl.flags);
+    if (sl.h_stage && !busy) (void)hipHostFree(sl.h_stage);
+    if (sl.flags && !busy) (void)hipHostFree(sl.flags);
   }
   if (p->d_stage) (void)hipFree(p->d_stage);
   if (p->d_part) (void)hipFree(p->d_part);
@@ -215,11 +227,15 @@ mla_status mla_plan_reserve(mla_plan_t p, int32_t max_batch, int64_t max_tokens,
   DeviceGuard g(p->device);
   if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
   const int64_t W = p->num_workers;
-  // Items: one per token, at most two more per worker where the balance cuts
-  // a token, and the cuts of rows longer than the longest item.
+  // Items: every token's visible keys (at most a row's keys, at most
+  // max_kv_indices pages) cut into pieces of at most kMaxItemTiles tiles, and
+  // at most two more per worker where the balance cuts a token.
   const int64_t max_keys = max_kv_indices * p->page_size;
-  const int64_t cap_items =
-      max_tokens + 2 * W + max_keys / (int64_t(mla::kTileKeys) * mla::kMaxItemTiles) + 8;
+  const int64_t item_keys = int64_t(mla::kTileKeys) * mla::kMaxItemTiles;
+  const int64_t per_token = 1 + (max_keys > 0 ? (max_keys - 1) / item_keys : 0);
+  if (per_token > (int64_t(1) << 40) / max_tokens)
+    return fail(MLA_E_INVALID, "reserved sizes too large");
+  const int64_t cap_items = max_tokens * per_token + 2 * W + 8;
   const int64_t cap_merges = std::min<int64_t>(max_tokens, cap_items);
   const size_t total =
       kAlign + align_up((W + 1) * sizeof(int32_t)) + align_up(cap_items * sizeof(mla::WorkItem)) +
@@ -231,7 +247,10 @@ mla_status mla_plan_reserve(mla_plan_t p, int32_t max_batch, int64_t max_tokens,
   hipError_t e = hipDeviceSynchronize();
   if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
   for (auto& sl : p->slot) {
-    if (sl.wait_seq > 0) wait_flags(p, sl);
+    if (sl.wait_seq > 0) {
+      const mla_status st = wait_flags(p, sl);
+      if (st != MLA_OK) return st;
+    }
     sl.pending = false;
     if (total > sl.cap) {
       if (sl.h_stage) (void)hipHostFree(sl.h_stage);
@@ -348,7 +367,10 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
     if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
     sl.pending = false;
   }
-  if (sl.wait_seq > 0) wait_flags(p, sl);
+  if (sl.wait_seq > 0) {
+    const mla_status st = wait_flags(p, sl);
+    if (st != MLA_OK) return st;
+  }
   if (total > sl.cap) {
     if (sl.h_stage) (void)hipHostFree(sl.h_stage);
     sl.h_stage = nullptr;
@@ -506,8 +528,13 @@ mla_status mla_run(mla_plan_t p, const void* q_nope, const void* q_pe, const voi
     hipError_t ce = hipStreamIsCapturing(stream, &cap);
     if (ce != hipSuccess) return hip_fail(ce, "hipStreamIsCapturing");
     capturing = cap != hipStreamCaptureStatusNone;
-    a.done_flags = sl.flags;
-    a.run_seq = ++p->run_seq;
+    // A captured run is never waited on, and stores no flag either: its
+    // replays would store its (older) sequence number after later eager
+    // runs had stored theirs, and a wait for those would never end.
+    if (!capturing) {
+      a.done_flags = sl.flags;
+      a.run_seq = ++p->run_seq;
+    }
     if (p->first_fast) {
       a.first_items = reinterpret_cast<const mla::WorkItem*>(d + p->off_first);
       a.first_pages = reinterpret_cast<const int32_t*>(d + p->off_fpages);

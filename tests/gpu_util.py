@@ -80,3 +80,15 @@ def sample_tokens(w, per_row=6, seed=0):
             pick.update(rng.integers(s, e, size=min(per_row, e - s)).tolist())
         out.extend(sorted(pick))
     return np.array(out, dtype=np.int64)
+
+
+def split_tokens(w, workers=None):
+    """Query tokens whose keys the planner splits over several work items
+    (their results go through the split-KV merge), for a plan on this
+    device (one worker per compute unit) unless `workers` is given."""
+    import paged_mla_attention_amd as pm
+    if workers is None:
+        workers = torch.cuda.get_device_properties(0).multi_processor_count
+    s = pm.schedule(w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_len, w.page_size,
+                    w.num_pages, w.num_heads, workers, causal=w.causal)
+    return np.unique(s["merges"][:, 0]).astype(np.int64)

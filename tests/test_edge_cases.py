@@ -49,6 +49,27 @@ def test_no_query_sees_a_key():
     assert_close(o, lse, o_ref, l_ref, "empty rows")
 
 
+@pytest.mark.parametrize("heads", [32, 64, 128])
+def test_empty_item_after_a_full_one_on_one_worker(heads):
+    """A query with no visible key right after a token with keys, on the same
+    worker (checked on the host schedule): the empty item's finish must not
+    disturb the previous item's output, for every wave count."""
+    import paged_mla_attention_amd as pm
+    rng = np.random.default_rng(31 + heads)
+    w = W.make_workload("empty_after", 0, [10, 0, 40, 0, 75, 0], [1, 1, 1, 1, 1, 1], heads, 16,
+                        rng=rng)
+    workers = torch.cuda.get_device_properties(0).multi_processor_count
+    s = pm.schedule(w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_len, 16, w.num_pages,
+                    heads, workers)
+    wi, items = s["worker_indptr"], s["items"]
+    pairs = [k for k in range(workers) for i in range(wi[k], wi[k + 1] - 1)
+             if items[i, 3] > items[i, 2] and items[i + 1, 3] == items[i + 1, 2]]
+    assert pairs, "no worker runs an empty item after one with keys"
+    o, lse = run_library(w)
+    o_ref, l_ref = oracle_of(w)
+    assert_close(o, lse, o_ref, l_ref, f"empty after full H={heads}")
+
+
 def test_empty_batch():
     import paged_mla_attention_amd as pm
     plan = pm.MLAPlan(16, 16)
@@ -80,3 +101,20 @@ def test_many_short_prefill_items_one_wave():
     o, lse = run_library(w)
     o_ref, l_ref = oracle_of(w)
     assert_close(o, lse, o_ref, l_ref, "short prefill H=24")
+
+
+def test_reserved_plan_takes_a_long_causal_prefix():
+    """A reserved plan sized for 516 tokens and a 64K-key row accepts a
+    causal prefill of 512 tokens over that row (every token re-walks the
+    prefix, in several items each) and matches the oracle on sampled tokens."""
+    import paged_mla_attention_amd as pm
+    from gpu_util import sample_tokens, split_tokens, to_dev_bf16
+    rng = np.random.default_rng(77)
+    w = W.make_workload("long_prefix", 0, [65536 + 512, 100], [512, 4], 16, 64, rng=rng)
+    plan = pm.MLAPlan(16, 64)
+    plan.reserve(2, w.num_tokens, int(w.kv_indptr[-1]))
+    o, lse = run_library(w, plan=plan)
+    plan.close()
+    toks = np.union1d(sample_tokens(w, per_row=4), split_tokens(w)[:16])
+    o_ref, l_ref = oracle_of(w, tokens=toks)
+    assert_close(o[toks], lse[toks], o_ref, l_ref, "reserved long causal prefix")

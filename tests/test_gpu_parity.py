@@ -9,7 +9,8 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_util import assert_close, from_dev_bf16, oracle_of, run_library, sample_tokens, to_dev_bf16
+from gpu_util import (assert_close, from_dev_bf16, oracle_of, run_library, sample_tokens,
+                      split_tokens, to_dev_bf16)
 
 torch = pytest.importorskip("torch")
 
@@ -124,22 +125,55 @@ def test_needle_causal_boundary(visible):
         assert np.abs(ow - needle).max() > 1.0
 
 
-def test_extreme_score_range_redo():
-    """Scores that grow by far more than 2^64 along the keys (the kernel's
-    reference-max redo path) still match the oracle."""
-    rng = np.random.default_rng(17)
-    L, H = 256, 32
-    w = W.make_workload("extreme", 0, [L], [1], H, 32, causal=False, rng=rng)
-    w.q_nope[:] = W.f32_to_bf16_bits(np.full((1, H, 512), 1.0, np.float32))
+def _redo_items(w, sched, c_of_key, qscale):
+    """Work items whose first tile's largest base-2 score sits more than 64
+    below a later score of the item (the kernel redoes such items with a new
+    reference maximum).  Scores here are qscale[h] * 512 * c_j * sm_scale."""
+    lens = w.kv_lens()
+    n = 0
+    for it in sched["items"]:
+        kb, ke = int(it[2]), int(it[3])
+        if ke <= kb:
+            continue
+        c = c_of_key[int(it[1])][kb:ke]
+        s2 = 512 * float(np.float32(w.sm_scale)) / np.log(2.0) * qscale.max()
+        if (c.max() - c[:32].max()) * s2 > 64:
+            n += 1
+    return n
+
+
+@pytest.mark.parametrize("heads", [32, 64, 128])
+@pytest.mark.parametrize("page_size", [32, 33])
+def test_extreme_score_range_redo(heads, page_size):
+    """Scores that jump by far more than 2^64 after a work item's first tile
+    (the kernel's reference-maximum redo path) still match the oracle, in
+    every kernel instantiation (one, two and four waves; tiles inside pages
+    and tiles spanning pages), for a decode row and a causal prefill row.
+    The schedule is checked on the host to contain items that take the redo."""
+    import paged_mla_attention_amd as pm
+    rng = np.random.default_rng(17 + heads + page_size)
+    kv, qo = [256, 300], [1, 24]
+    w = W.make_workload("extreme", 0, kv, qo, heads, page_size, causal=True, rng=rng)
+    qscale = 1.0 + np.arange(heads) / heads  # heads differ
+    q = np.broadcast_to(qscale[None, :, None], (w.num_tokens, heads, 512)).astype(np.float32)
+    w.q_nope[:] = W.f32_to_bf16_bits(q)
     w.q_pe[:] = 0
-    # key j's ckv = c_j * ones, c_j grows so that scores jump past the first tile
-    for j in range(L):
-        c = 0.01 if j < 32 else (0.5 if j < 200 else 1.5)
-        w.kv_cache[w.kv_indices[j // 32], j % 32, :512] = W.f32_to_bf16_bits(
-            np.full(512, c, np.float32))
-    o, lse = run_library(w)
+    c_of_key = []
+    for b, L in enumerate(kv):
+        c = np.where(np.arange(L) < 32, 0.01, np.where(np.arange(L) < 40, 0.5, 3.0))
+        c_of_key.append(c)
+        for j in range(L):
+            pg = w.kv_indices[w.kv_indptr[b] + j // page_size]
+            w.kv_cache[pg, j % page_size, :512] = W.f32_to_bf16_bits(
+                np.full(512, c[j], np.float32))
+    plan = pm.MLAPlan(heads, page_size)
+    o, lse = run_library(w, plan=plan)
+    sched = pm.schedule(w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_len, page_size,
+                        w.num_pages, heads, plan.stats()["num_workers"], causal=True)
+    plan.close()
+    assert _redo_items(w, sched, c_of_key, qscale) > 0, "no item reaches the redo branch"
     o_ref, l_ref = oracle_of(w)
-    assert_close(o, lse, o_ref, l_ref, "extreme")
+    assert_close(o, lse, o_ref, l_ref, f"extreme H={heads} P={page_size}")
 
 
 def test_replan_reuses_buffers():
@@ -178,7 +212,7 @@ def test_long_decode_full():
 def test_chunked_prefill_sampled():
     w = W.chunked_prefill()
     o, lse = run_library(w)
-    toks = sample_tokens(w, per_row=5)
+    toks = np.union1d(sample_tokens(w, per_row=5), split_tokens(w))
     o_ref, l_ref = oracle_of(w, tokens=toks)
     assert_close(o[toks], lse[toks], o_ref, l_ref, "chunked prefill")
 
@@ -200,7 +234,7 @@ def test_mixed_with_extra_segment_merge():
     o_m, s_m = pm.merge_state(o_main, s_main, o_ext, s_ext)
     torch.cuda.synchronize()
     plan.close()
-    toks = sample_tokens(w, per_row=3)
+    toks = np.union1d(sample_tokens(w, per_row=3), split_tokens(w))
     # main segment alone
     o_ref, l_ref = oracle_of(w, tokens=toks)
     assert_close(from_dev_bf16(o_main)[toks], s_main.cpu().numpy()[toks], o_ref, l_ref, "mixed main")

@@ -61,6 +61,18 @@ def test_graph_replays_match_eager(shape):
         plan.run(qn, qp, kv, out=out, lse=lse)
         torch.cuda.synchronize()
         assert torch.equal(out, ref_o)
+    # A replay after the eager runs, then two fresh plans (each refills a
+    # staging slot, waiting for the runs that read it) and the plan's
+    # release: none of them may wait on the captured run.
+    g.replay()
+    torch.cuda.synchronize()
+    last = w.kv_last_page_len.copy()
+    for k in range(2):
+        last[0] = w.kv_last_page_len[0] - 1 - k
+        plan.plan(w.qo_indptr, w.kv_indptr, w.kv_indices, last, causal=True,
+                  sm_scale=w.sm_scale, num_cache_pages=w.num_pages)
+        plan.run(qn, qp, kv, out=out, lse=lse)
+    torch.cuda.synchronize()
     plan.close()
     assert stats["num_workers"] > 0
 

@@ -190,3 +190,43 @@ def test_planner_under_sanitizers(tmp_path):
     r = subprocess.run([exe, "300"], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "ok" in r.stdout
+
+
+def test_slot_wait_has_a_deadline(tmp_path):
+    """The host's wait for the kernels to release a staging slot ends at its
+    deadline when a flag never arrives (and returns at once when they have)."""
+    import shutil
+    import subprocess
+    if shutil.which("g++") is None:
+        pytest.skip("g++ not available")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    exe = str(tmp_path / "host_wait_check")
+    r = subprocess.run(["g++", "-std=c++17", "-O1", "-pthread", "-I",
+                        os.path.join(root, "paged_mla_attention_amd", "csrc"),
+                        os.path.join(root, "tests", "host_wait_check.cpp"), "-o", exe],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and "ok" in r.stdout, r.stdout + r.stderr
+
+
+def test_item_count_within_reserved_bound(host_lib):
+    """A causal prefill over a 64K-key prefix: every query token re-walks
+    its row's prefix, so the item count grows with tokens times the prefix's
+    item cuts.  It stays within what a reserved plan sizes for:
+    tokens * (1 + (max_keys - 1) // (32 * 1024)) + 2 * workers + 8."""
+    P, workers = 64, 256
+    kv_lens, qo_lens = [65536 + 512, 100], [512, 4]
+    pages = [(L + P - 1) // P for L in kv_lens]
+    kv_indptr = np.concatenate([[0], np.cumsum(pages)]).astype(np.int32)
+    qo_indptr = np.concatenate([[0], np.cumsum(qo_lens)]).astype(np.int32)
+    kv_indices = np.random.default_rng(3).permutation(kv_indptr[-1]).astype(np.int32)
+    last = np.array([L - (n - 1) * P for L, n in zip(kv_lens, pages)], np.int32)
+    s = schedule(qo_indptr, kv_indptr, kv_indices, last, P, int(kv_indptr[-1]), 16, workers,
+                 causal=True, lib_path=host_lib)
+    T = int(qo_indptr[-1])
+    max_keys = int(kv_indptr[-1]) * P
+    bound = T * (1 + (max_keys - 1) // (TILE * 1024)) + 2 * workers + 8
+    assert s["items"].shape[0] <= bound
+    # the bound a reserved plan used to make (one cut per cached key) is exceeded
+    assert s["items"].shape[0] > T + 2 * workers + max_keys // (TILE * 1024) + 8
