@@ -205,6 +205,47 @@ mla_status mla_merge_state(const void* v_a, const float* s_a, const void* v_b,
                            const float* s_b, void* v_out, float* s_out,
                            int64_t num_tokens, int32_t num_heads, mla_stream_t stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): mla_plan + mla_run in one
+ * call that allocates nothing and reads the page table from DEVICE memory.
+ *
+ * qo_indptr [batch+1], kv_indptr [batch+1], kv_indices [num_kv_indices] and
+ * kv_last_page_len [batch] are device int32 arrays with the layout and rules
+ * of mla_plan; num_tokens must equal qo_indptr[batch] and max_kv_len must
+ * bound the keys of every row (both host values the caller knows from its
+ * tensor shapes and sequence limits).  q_nope, q_pe, kv_cache, out and lse
+ * are as for mla_run; `lse` may be NULL.  Runs on the current HIP device.
+ *
+ * Three kernels are enqueued on `stream` (a planner that validates the page
+ * table and splits the work on the device, the attention kernel and the
+ * split-KV merge); there is no allocation, no host synchronisation and no
+ * memset, so the call may be captured in a HIP graph.  The schedule, its
+ * temporaries and the split-KV partials live in one fixed device array of
+ * about 81 MiB per GPU, allocated with the library's code object on each GPU
+ * it runs on and held until the process ends.  Every call on a GPU shares
+ * that array and leaves its contents behind: calls that overlap on one GPU
+ * (other streams, other threads) race and must be ordered by the caller.
+ *
+ * Limits: batch <= 8192 rows, num_tokens <= 8192, and a worst case for rows of
+ * max_kv_len keys within the workspace: num_tokens * (1 + c) + 256 work items
+ * <= 16384 and 512 + num_tokens * (c ? c + 1 : 0) split partials <=
+ * 80 MiB / (num_heads * 1028 B), where c = (ceil(max_kv_len / 32) - 1) / 1024
+ * for max_kv_len > 32768 keys, else 0 (at 128 heads: 637 partials).  Calls
+ * beyond them fail with MLA_E_INVALID and a message naming the limit.  A
+ * page table that breaks the rules of mla_plan (checked on the device,
+ * including max_kv_len) yields zero output and -inf LSE for every token.
+ *
+ * Errors: MLA_E_INVALID for sizes beyond the limits, NULL pointers or a bad
+ * scalar; MLA_E_UNSUPPORTED for num_heads outside [1, 128]; MLA_E_HIP when
+ * the symbol lookup or a launch fails. */
+mla_status mla_run_noalloc(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                           const int32_t* kv_indices, const int32_t* kv_last_page_len,
+                           int32_t batch, int64_t num_tokens, int64_t num_kv_indices,
+                           int32_t causal, float sm_scale, int64_t num_cache_pages,
+                           int32_t max_kv_len, int32_t num_heads, int32_t page_size,
+                           const void* q_nope, const void* q_pe, const void* kv_cache,
+                           void* out, float* lse, mla_stream_t stream);
+
 /* Release a plan and everything it owns.  Waits for the plan's pending
  * copy; the caller must make sure no enqueued mla_run on it is still
  * executing.  NULL is ignored. */

@@ -27,6 +27,7 @@ __all__ = [
     "MLAPlan", "mla_plan_create", "mla_plan", "mla_run", "mla_append_kv", "mla_merge_state",
     "mla_absorb_query", "mla_up_project", "absorb_query", "up_project",
     "mla_plan_destroy", "mla_plan_stats", "merge_state", "schedule", "append_rows", "library",
+    "mla_run_noalloc", "run_noalloc",
 ]
 
 
@@ -302,6 +303,54 @@ def merge_state(v_a, s_a, v_b, s_b, v_out=None, s_out=None, stream=None):
     ]
     mla_merge_state(*ptrs, T, H, _stream_handle(stream))
     return v_out, s_out
+
+
+def mla_run_noalloc(qo_indptr: int, kv_indptr: int, kv_indices: int, kv_last_page_len: int,
+                    batch: int, num_tokens: int, num_kv_indices: int, causal: bool,
+                    sm_scale: float, num_cache_pages: int, max_kv_len: int, num_heads: int,
+                    page_size: int, q_nope: int, q_pe: int, kv_cache: int, out: int, lse: int,
+                    stream: Optional[int]) -> None:
+    lib = library()
+    _native.check(lib, lib.mla_run_noalloc(qo_indptr, kv_indptr, kv_indices, kv_last_page_len,
+                                           batch, num_tokens, num_kv_indices, 1 if causal else 0,
+                                           sm_scale, num_cache_pages, max_kv_len, num_heads,
+                                           page_size, q_nope, q_pe, kv_cache, out, lse, stream))
+
+
+def run_noalloc(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, q_nope, q_pe, kv_cache,
+                page_size: int, max_kv_len: int, causal: bool = True, sm_scale: float = None,
+                out=None, lse=None, return_lse: bool = False, stream=None):
+    """mla_run_noalloc with torch tensors: the page table as int32 GPU
+    tensors, everything else as for MLAPlan.run.  Allocates only what the
+    caller did not pass (out, lse); the library allocates nothing."""
+    import torch
+    if sm_scale is None:
+        raise ValueError("sm_scale is required")
+    if q_nope.dim() != 3 or q_nope.shape[-1] != KV_LORA_RANK:
+        raise ValueError("q_nope must be [T, H, 512]")
+    T, H = int(q_nope.shape[0]), int(q_nope.shape[1])
+    B = int(qo_indptr.shape[0]) - 1
+    nnz = int(kv_indices.shape[0])
+    if kv_cache.dim() != 3 or kv_cache.shape[1:] != (page_size, KV_LORA_RANK + QK_ROPE_HEAD_DIM):
+        raise ValueError("kv_cache must be [pages, page_size, 576]")
+    pages = int(kv_cache.shape[0])
+    if out is None:
+        out = torch.empty((T, H, KV_LORA_RANK), dtype=torch.bfloat16, device=q_nope.device)
+    if lse is None and return_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q_nope.device)
+    mla_run_noalloc(
+        _dev_ptr(qo_indptr, "qo_indptr", torch.int32, (B + 1,)),
+        _dev_ptr(kv_indptr, "kv_indptr", torch.int32, (B + 1,)),
+        _dev_ptr(kv_indices, "kv_indices", torch.int32, (nnz,)) if nnz else None,
+        _dev_ptr(kv_last_page_len, "kv_last_page_len", torch.int32, (B,)),
+        B, T, nnz, causal, float(sm_scale), pages, int(max_kv_len), H, page_size,
+        _dev_ptr(q_nope, "q_nope", torch.bfloat16, (T, H, KV_LORA_RANK)),
+        _dev_ptr(q_pe, "q_pe", torch.bfloat16, (T, H, QK_ROPE_HEAD_DIM)),
+        _dev_ptr(kv_cache, "kv_cache", torch.bfloat16, tuple(kv_cache.shape)),
+        _dev_ptr(out, "out", torch.bfloat16, (T, H, KV_LORA_RANK)),
+        _dev_ptr(lse, "lse", torch.float32, (T, H)) if lse is not None else None,
+        _stream_handle(stream))
+    return (out, lse) if return_lse else out
 
 
 # ----------------------------------------------------------------------------

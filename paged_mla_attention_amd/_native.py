@@ -26,6 +26,9 @@ SIGNATURES = {
     "mla_up_project": (c_int32, [c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_void_p]),
     "mla_merge_state": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_int64, c_int32, c_void_p]),
+    "mla_run_noalloc": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int64,
+                                  c_int64, c_int32, c_float, c_int64, c_int32, c_int32, c_int32,
+                                  c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "mla_plan_destroy": (None, [c_void_p]),
     "mla_plan_stats": (c_int32, [c_void_p, _i32p, _i64p, _i64p, _i64p]),
     "mla_status_str": (c_char_p, [c_int32]),

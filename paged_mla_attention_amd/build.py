@@ -24,7 +24,7 @@ LIB = os.path.join(PKG, "libmla.so")
 HOST_LIB = os.path.join(PKG, "libmla_host.so")
 
 HIP_SOURCES = ["planner.cpp", "capi.cpp", "attention.hip", "merge.hip", "append.hip",
-               "projection.hip"]
+               "projection.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 
