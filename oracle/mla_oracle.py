@@ -50,6 +50,17 @@ by ``W_UV``): per head, ``q_abs[t,h,:] = q_nope[t,h,:] @ W_UK[h]`` with
 ``W_UV [H, 512, d_v]``; reading (the pages state only the 192-wide scale):
 ``d_nope = d_v = 128``.
 
+An fp8 latent cache (the wrapper's ``plan`` takes a ``kv_dtype``, default
+``None``, i.e. the bf16 of ``dtype``; the pages name no fp8 format or
+scale).  Reading: the cache holds OCP FP8 E4M3 codes (1 sign bit, 4
+exponent bits with bias 7, 3 mantissa bits, subnormals, no infinities, the
+all-ones magnitude is NaN, largest finite 448) and one fp32 dequantisation
+scale for the whole cache, shared by ckv and kpe: a cached value is
+``decode(code) * kv_scale``.  Appending a bf16 row quantises
+``fp32(x / kv_scale)`` (IEEE fp32 division) to the nearest code, ties to the
+even mantissa, saturating at +-448.  Attention over such a cache is the
+attention above over the dequantised values.
+
 Parity pins: every function here is checked by the CPU tests against
 something other than itself (brute-force non-absorbed attention, page
 permutation invariance, the two-segment merge identity, the single-key and
@@ -314,3 +325,75 @@ def up_project(o, w_uv):
     """The latent output brought to the value heads, ``o @ W_UV`` per head:
     ``[T, H, 512] x [H, 512, 128] -> [T, H, 128]`` (fp64)."""
     return head_matmul(o, w_uv)
+
+
+# ---------------------------------------------------------------------------
+# fp8 (OCP E4M3) latent cache
+# ---------------------------------------------------------------------------
+
+FP8_E4M3_MAX = 448.0
+
+
+def fp8_e4m3_decode(codes) -> np.ndarray:
+    """fp64 values of FP8 E4M3 codes (uint8), by the format's definition:
+    sign s, exponent field e (bias 7), mantissa field m; e = 0 gives the
+    subnormal ``m / 8 * 2**-6``, otherwise ``(1 + m / 8) * 2**(e - 7)``;
+    e = 15 with m = 7 is NaN (there are no infinities)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    out = sign * mag
+    return np.where((e == 15) & (m == 7), np.nan, out)
+
+
+def fp8_e4m3_encode(x) -> np.ndarray:
+    """FP8 E4M3 code (uint8) nearest to each finite value of ``x``, ties to
+    the even code, magnitudes beyond 448 saturated to 448.
+
+    Written as a search over the 127 non-negative finite codes (their
+    values increase with the code): the two neighbours of |x| and the
+    distance to each decide, a tie goes to the code with an even mantissa."""
+    v = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(v)):
+        raise ValueError("fp8 encode takes finite values only")
+    grid = fp8_e4m3_decode(np.arange(127, dtype=np.uint8))  # 0 .. 448, increasing
+    a = np.minimum(np.abs(v), FP8_E4M3_MAX)
+    hi = np.searchsorted(grid, a, side="left")  # first grid value >= a
+    hi = np.minimum(hi, 126)
+    lo = np.where(grid[hi] == a, hi, np.maximum(hi - 1, 0))
+    d_lo, d_hi = a - grid[lo], grid[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0) & (hi != lo))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(np.signbit(v) & (code != 0), code | 0x80, code).astype(np.uint8)
+
+
+def fp8_quantize_rows(x_bits, kv_scale) -> np.ndarray:
+    """Codes of bf16 values (uint16 bits) stored in an fp8 cache with scale
+    ``kv_scale``: the fp32 quotient ``x / kv_scale`` rounded to a code."""
+    q = (widen(x_bits).astype(np.float32) / np.float32(kv_scale)).astype(np.float64)
+    return fp8_e4m3_encode(q)
+
+
+def dequantize_cache(kv_cache_fp8, kv_scale) -> np.ndarray:
+    """The values an fp8 cache holds, fp64: ``decode(code) * kv_scale``."""
+    return fp8_e4m3_decode(kv_cache_fp8) * float(np.float32(kv_scale))
+
+
+def attention_fp8(q_nope, q_pe, kv_cache_fp8, qo_indptr, kv_indptr, kv_indices,
+                  kv_last_page_len, page_size, causal, sm_scale, kv_scale, tokens=None):
+    """Paged latent attention over an fp8 cache (codes ``[pages, P, 576]``
+    uint8): the attention above on the dequantised cache."""
+    return attention(q_nope, q_pe, dequantize_cache(kv_cache_fp8, kv_scale), qo_indptr,
+                     kv_indptr, kv_indices, kv_last_page_len, page_size, causal, sm_scale,
+                     tokens=tokens)
+
+
+def append_kv_fp8(kv_cache_fp8, ckv, kpe, qo_indptr, kv_indptr, kv_indices, kv_last_page_len,
+                  page_size, kv_scale):
+    """The fp8 cache after this step's bf16 rows are quantised and written
+    to the slots ``append_kv`` gives them (a new array)."""
+    return append_kv(kv_cache_fp8, fp8_quantize_rows(ckv, kv_scale),
+                     fp8_quantize_rows(kpe, kv_scale), qo_indptr, kv_indptr, kv_indices,
+                     kv_last_page_len, page_size)

@@ -12,7 +12,7 @@ import sys
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-PIN_TESTS = ["test_oracle.py", "test_append_oracle.py"]
+PIN_TESTS = ["test_oracle.py", "test_append_oracle.py", "test_fp8_oracle.py"]
 
 # (name, exact text in oracle/mla_oracle.py, replacement)
 MUTATIONS = [
@@ -30,6 +30,14 @@ MUTATIONS = [
     ("append_off_by_one", "            j = L - Q + i\n", "            j = L - Q + i - 1\n"),
     ("projection_head_order", 'np.einsum("thk,hkn->thn", xf, wf)',
      'np.einsum("thk,hkn->thn", xf, wf[::-1])'),
+    ("fp8_exponent_bias", "np.exp2(e - 7.0)", "np.exp2(e - 8.0)"),
+    ("fp8_subnormal_step", "m / 8.0 * 2.0 ** -6", "m / 8.0 * 2.0 ** -7"),
+    ("fp8_ties_away_from_zero", "((d_hi == d_lo) & (hi % 2 == 0) & (hi != lo))",
+     "((d_hi == d_lo) & (hi != lo))"),
+    ("fp8_scale_dropped", "return fp8_e4m3_decode(kv_cache_fp8) * float(np.float32(kv_scale))",
+     "return fp8_e4m3_decode(kv_cache_fp8)"),
+    ("fp8_quantize_multiplies", "astype(np.float32) / np.float32(kv_scale)",
+     "astype(np.float32) * np.float32(kv_scale)"),
 ]
 
 
