@@ -58,7 +58,7 @@ all-ones magnitude is NaN, largest finite 448) and one fp32 dequantisation
 scale for the whole cache, shared by ckv and kpe: a cached value is
 ``decode(code) * kv_scale``.  Appending a bf16 row quantises
 ``fp32(x / kv_scale)`` (IEEE fp32 division) to the nearest code, ties to the
-even mantissa, saturating at +-448.  Attention over such a cache is the
+even mantissa, saturating at +-448, keeping the sign of zero.  Attention over such a cache is the
 attention above over the dequantised values.
 
 Parity pins: every function here is checked by the CPU tests against
@@ -350,7 +350,8 @@ def fp8_e4m3_decode(codes) -> np.ndarray:
 
 def fp8_e4m3_encode(x) -> np.ndarray:
     """FP8 E4M3 code (uint8) nearest to each finite value of ``x``, ties to
-    the even code, magnitudes beyond 448 saturated to 448.
+    the even code, magnitudes beyond 448 saturated to 448; the sign is kept,
+    also for a value that rounds to zero (-0).
 
     Written as a search over the 127 non-negative finite codes (their
     values increase with the code): the two neighbours of |x| and the
@@ -366,7 +367,7 @@ def fp8_e4m3_encode(x) -> np.ndarray:
     d_lo, d_hi = a - grid[lo], grid[hi] - a
     pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0) & (hi != lo))
     code = np.where(pick_hi, hi, lo).astype(np.uint8)
-    return np.where(np.signbit(v) & (code != 0), code | 0x80, code).astype(np.uint8)
+    return np.where(np.signbit(v), code | 0x80, code).astype(np.uint8)
 
 
 def fp8_quantize_rows(x_bits, kv_scale) -> np.ndarray:

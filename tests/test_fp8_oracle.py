@@ -36,9 +36,9 @@ def test_decode_closed_forms():
 
 
 def test_encode_roundtrips_every_finite_code():
-    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF, 0x80)], np.uint8)
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
     assert np.array_equal(oracle.fp8_e4m3_encode(oracle.fp8_e4m3_decode(codes)), codes)
-    assert oracle.fp8_e4m3_encode(np.array([-0.0]))[0] == 0  # -0 stores as +0
+    assert oracle.fp8_e4m3_encode(np.array([-0.0, -1e-9]))[1] == 0x80  # signed zero
 
 
 def test_encode_ties_and_near_ties_match_torch():
@@ -51,8 +51,6 @@ def test_encode_ties_and_near_ties_match_torch():
     vals = np.concatenate([near, -near, grid, [464.0]]).astype(np.float32)
     ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     ours = oracle.fp8_e4m3_encode(vals.astype(np.float64))
-    # torch keeps the sign of a value that rounds to zero; the oracle stores +0
-    ref = np.where((ref & 0x7F) == 0, 0, ref)
     assert np.array_equal(ours, ref)
 
 
@@ -61,7 +59,6 @@ def test_encode_random_matches_torch():
     vals = np.concatenate([rng.standard_normal(20000) * s for s in (1e-3, 0.1, 1, 30, 150)])
     vals = np.clip(vals, -448, 448).astype(np.float32)
     ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
-    ref = np.where((ref & 0x7F) == 0, 0, ref)
     assert np.array_equal(oracle.fp8_e4m3_encode(vals.astype(np.float64)), ref)
 
 
@@ -78,7 +75,6 @@ def test_quantize_rows_is_fp32_quotient_rounded():
     for s in (1.0, 0.0625, 3.0, 0.37):
         q = (torch.from_numpy(xf) / torch.tensor(np.float32(s))).clamp(-448, 448)
         ref = q.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
-        ref = np.where((ref & 0x7F) == 0, 0, ref)
         assert np.array_equal(oracle.fp8_quantize_rows(x, s), ref), s
 
 
