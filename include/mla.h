@@ -149,6 +149,23 @@ mla_status mla_plan_reserve(mla_plan_t plan, int32_t max_batch, int64_t max_toke
 mla_status mla_run(mla_plan_t plan, const void* q_nope, const void* q_pe,
                    const void* kv_cache, void* out, float* lse, mla_stream_t stream);
 
+/* mla_run over an fp8 latent cache (FlashInferMLAWrapper.plan takes a
+ * kv_dtype; the pages name no fp8 format, and this library reads one as):
+ * kv_cache_fp8 is [num_cache_pages, page_size, 576] bytes of OCP FP8 E4M3
+ * codes (sign, 4 exponent bits with bias 7, 3 mantissa bits, subnormals,
+ * largest finite 448, no infinities), ckv then kpe, and a cached value is
+ * decode(code) * kv_scale for the one fp32 scale of the whole cache.  The
+ * result is the attention of mla_run over those values: q, out and lse keep
+ * the layouts and dtypes of mla_run.  The codes are converted exactly to
+ * bf16 on the GPU and kv_scale is applied in fp32 to the scores and the
+ * normalised output.  The same plan serves bf16 and fp8 runs.
+ *
+ * Errors: those of mla_run, and MLA_E_INVALID for a kv_scale that is not
+ * finite and positive. */
+mla_status mla_run_fp8(mla_plan_t plan, const void* q_nope, const void* q_pe,
+                       const void* kv_cache_fp8, float kv_scale, void* out, float* lse,
+                       mla_stream_t stream);
+
 /* Write this step's latent rows into the cache before attention reads it
  * (page "mstar.engine.resources.attn.base", AttentionManager.requires_kv_write:
  * a layer writes the step's K/V through the KV resource, then calls run).
@@ -170,6 +187,14 @@ mla_status mla_run(mla_plan_t plan, const void* q_nope, const void* q_pe,
  * the launch fails. */
 mla_status mla_append_kv(mla_plan_t plan, const void* ckv, const void* kpe, void* kv_cache,
                          mla_stream_t stream);
+
+/* mla_append_kv into an fp8 cache (the layout of mla_run_fp8): each bf16
+ * value x becomes the E4M3 code nearest to the fp32 quotient x / kv_scale,
+ * ties to the even mantissa, magnitudes beyond 448 saturated to 448, the
+ * sign of zero kept.  Same slots, fences and errors as mla_append_kv, plus
+ * MLA_E_INVALID for a kv_scale that is not finite and positive. */
+mla_status mla_append_kv_fp8(mla_plan_t plan, const void* ckv, const void* kpe,
+                             void* kv_cache_fp8, float kv_scale, mla_stream_t stream);
 
 /* The projections either side of the kernel (module description of the
  * flashinfer_mla page: the query entering the kernel is absorbed,

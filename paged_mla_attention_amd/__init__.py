@@ -27,7 +27,7 @@ __all__ = [
     "MLAPlan", "mla_plan_create", "mla_plan", "mla_run", "mla_append_kv", "mla_merge_state",
     "mla_absorb_query", "mla_up_project", "absorb_query", "up_project",
     "mla_plan_destroy", "mla_plan_stats", "merge_state", "schedule", "append_rows", "library",
-    "mla_run_noalloc", "run_noalloc",
+    "mla_run_noalloc", "run_noalloc", "mla_run_fp8", "mla_append_kv_fp8",
 ]
 
 
@@ -110,10 +110,37 @@ def mla_run(handle: int, q_nope_ptr: int, q_pe_ptr: int, kv_cache_ptr: int, out_
                                    lse_ptr, stream))
 
 
+def mla_run_fp8(handle: int, q_nope_ptr: int, q_pe_ptr: int, kv_cache_ptr: int, kv_scale: float,
+                out_ptr: int, lse_ptr: Optional[int], stream: int) -> None:
+    lib = library()
+    _native.check(lib, lib.mla_run_fp8(handle, q_nope_ptr, q_pe_ptr, kv_cache_ptr,
+                                       float(kv_scale), out_ptr, lse_ptr, stream))
+
+
 def mla_append_kv(handle: int, ckv_ptr: int, kpe_ptr: int, kv_cache_ptr: int,
                   stream: int) -> None:
     lib = library()
     _native.check(lib, lib.mla_append_kv(handle, ckv_ptr, kpe_ptr, kv_cache_ptr, stream))
+
+
+def mla_append_kv_fp8(handle: int, ckv_ptr: int, kpe_ptr: int, kv_cache_ptr: int,
+                      kv_scale: float, stream: int) -> None:
+    lib = library()
+    _native.check(lib, lib.mla_append_kv_fp8(handle, ckv_ptr, kpe_ptr, kv_cache_ptr,
+                                             float(kv_scale), stream))
+
+
+def _kv_dtype(kv_dtype):
+    """The cache dtype a plan is made for: None / bfloat16 (the default) or
+    an fp8 E4M3 cache ("fp8_e4m3" or torch.float8_e4m3fn)."""
+    if kv_dtype is None:
+        return "bf16"
+    name = str(kv_dtype).replace("torch.", "")
+    if name in ("bf16", "bfloat16"):
+        return "bf16"
+    if name in ("fp8_e4m3", "float8_e4m3fn", "e4m3"):
+        return "fp8_e4m3"
+    raise ValueError(f"unsupported kv_dtype {kv_dtype!r} (bf16 or fp8_e4m3)")
 
 
 def mla_merge_state(v_a: int, s_a: int, v_b: int, s_b: int, v_out: int, s_out: int,
@@ -161,6 +188,7 @@ class MLAPlan:
         self._h = mla_plan_create(self.device, self.num_heads, kv_lora_rank, qk_rope_head_dim,
                                   self.page_size)
         self._planned = None
+        self.kv_dtype = "bf16"
 
     def reserve(self, max_batch: int, max_tokens: int, max_kv_indices: int) -> None:
         """Fix the plan's capacity so that a captured ``run`` stays valid while
@@ -173,16 +201,35 @@ class MLAPlan:
 
     def plan(self, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, causal: bool = True,
              sm_scale: float = 192.0 ** -0.5, num_cache_pages: Optional[int] = None,
-             stream=None) -> None:
+             stream=None, kv_dtype=None) -> None:
+        """``kv_dtype`` None (bf16 cache) or "fp8_e4m3" (E4M3 codes with one
+        fp32 scale, given to ``run`` / ``append_kv`` as ``kv_scale``)."""
         qo = _host_i32(qo_indptr)
         if num_cache_pages is None:
             raise ValueError("num_cache_pages is required (page ids are validated against it)")
+        dt = _kv_dtype(kv_dtype)
         mla_plan(self._h, qo, kv_indptr, kv_indices, kv_last_page_len, causal, sm_scale,
                  num_cache_pages, _stream_handle(stream))
         self._planned = (int(qo[-1]), int(num_cache_pages))
+        self.kv_dtype = dt
+
+    def _cache_ptr(self, kv_cache, pages, kv_scale):
+        import torch
+        if kv_cache.dim() != 3 or kv_cache.shape[0] < pages:
+            raise ValueError(f"kv_cache must be [>= {pages}, page_size, 576]")
+        shape = (kv_cache.shape[0], self.page_size, KV_LORA_RANK + QK_ROPE_HEAD_DIM)
+        if self.kv_dtype == "bf16":
+            if kv_scale is not None:
+                raise ValueError("kv_scale is for an fp8 cache (plan with kv_dtype='fp8_e4m3')")
+            return _dev_ptr(kv_cache, "kv_cache", torch.bfloat16, shape)
+        if kv_scale is None:
+            raise ValueError("an fp8 cache needs kv_scale")
+        if kv_cache.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise ValueError(f"an fp8 cache is uint8 or float8_e4m3fn, got {kv_cache.dtype}")
+        return _dev_ptr(kv_cache, "kv_cache", kv_cache.dtype, shape)
 
     def run(self, q_nope, q_pe, kv_cache, return_lse: bool = False, out=None, lse=None,
-            stream=None):
+            stream=None, kv_scale: Optional[float] = None):
         import torch
         if self._planned is None:
             raise RuntimeError("run() before plan()")
@@ -190,12 +237,9 @@ class MLAPlan:
         H = self.num_heads
         if getattr(self, "_reserved_tokens", None):
             T = self._reserved_tokens  # tensors sized for the reserved capacity
-        if kv_cache.dim() != 3 or kv_cache.shape[0] < pages:
-            raise ValueError(f"kv_cache must be [>= {pages}, page_size, 576]")
+        kv = self._cache_ptr(kv_cache, pages, kv_scale)
         qn = _dev_ptr(q_nope, "q_nope", torch.bfloat16, (T, H, KV_LORA_RANK))
         qp = _dev_ptr(q_pe, "q_pe", torch.bfloat16, (T, H, QK_ROPE_HEAD_DIM))
-        kv = _dev_ptr(kv_cache, "kv_cache", torch.bfloat16,
-                      (kv_cache.shape[0], self.page_size, KV_LORA_RANK + QK_ROPE_HEAD_DIM))
         if out is None:
             out = torch.empty((T, H, KV_LORA_RANK), dtype=torch.bfloat16, device=q_nope.device)
         op = _dev_ptr(out, "out", torch.bfloat16, (T, H, KV_LORA_RANK))
@@ -204,25 +248,29 @@ class MLAPlan:
             if lse is None:
                 lse = torch.empty((T, H), dtype=torch.float32, device=q_nope.device)
             lp = _dev_ptr(lse, "lse", torch.float32, (T, H))
-        mla_run(self._h, qn, qp, kv, op, lp, _stream_handle(stream))
+        if self.kv_dtype == "bf16":
+            mla_run(self._h, qn, qp, kv, op, lp, _stream_handle(stream))
+        else:
+            mla_run_fp8(self._h, qn, qp, kv, kv_scale, op, lp, _stream_handle(stream))
         return (out, lse) if (return_lse or lp is not None) else out
 
-    def append_kv(self, ckv, kpe, kv_cache, stream=None) -> None:
+    def append_kv(self, ckv, kpe, kv_cache, stream=None, kv_scale: Optional[float] = None) -> None:
         """Write this step's latent rows (``ckv [T, 512]``, ``kpe [T, 64]``
         bf16) into ``kv_cache`` in place: token i of a row with Q tokens and
         L keys becomes the row's key L - Q + i (mirrors the KV write a layer
-        makes before ``run``)."""
+        makes before ``run``).  An fp8 cache stores the E4M3 codes of
+        ``x / kv_scale``."""
         import torch
         if self._planned is None:
             raise RuntimeError("append_kv() before plan()")
         T, pages = self._planned
-        if kv_cache.dim() != 3 or kv_cache.shape[0] < pages:
-            raise ValueError(f"kv_cache must be [>= {pages}, page_size, 576]")
+        kv = self._cache_ptr(kv_cache, pages, kv_scale)
         cp = _dev_ptr(ckv, "ckv", torch.bfloat16, (T, KV_LORA_RANK))
         pp = _dev_ptr(kpe, "kpe", torch.bfloat16, (T, QK_ROPE_HEAD_DIM))
-        kv = _dev_ptr(kv_cache, "kv_cache", torch.bfloat16,
-                      (kv_cache.shape[0], self.page_size, KV_LORA_RANK + QK_ROPE_HEAD_DIM))
-        mla_append_kv(self._h, cp, pp, kv, _stream_handle(stream))
+        if self.kv_dtype == "bf16":
+            mla_append_kv(self._h, cp, pp, kv, _stream_handle(stream))
+        else:
+            mla_append_kv_fp8(self._h, cp, pp, kv, kv_scale, _stream_handle(stream))
 
     def stats(self) -> dict:
         return mla_plan_stats(self._h)

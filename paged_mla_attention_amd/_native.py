@@ -21,7 +21,10 @@ SIGNATURES = {
     "mla_plan": (c_int32, [c_void_p, _i32p, _i32p, _i32p, _i32p, c_int32, c_int32, c_float,
                            c_int64, c_void_p]),
     "mla_run": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "mla_run_fp8": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_float, c_void_p,
+                              c_void_p, c_void_p]),
     "mla_append_kv": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "mla_append_kv_fp8": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_float, c_void_p]),
     "mla_absorb_query": (c_int32, [c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_void_p]),
     "mla_up_project": (c_int32, [c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_void_p]),
     "mla_merge_state": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,

@@ -149,19 +149,49 @@ __device__ __forceinline__ int opaque(int v) {
   return v;
 }
 
-template <int NW, bool kTileInPage>
+// An fp8 cache (kFp8): a tile's 32 latent rows are 32 x 576 E4M3 codes
+// (18 KiB).  Each wave DMAs the raw codes of the latent columns it owns in
+// P . V ([512w/NW, 512(w+1)/NW), two 16-column chunks of the 32 keys per
+// 1 KiB instruction) and a quarter of the kpe columns (one 16-column chunk
+// per 512-byte, half-wave instruction) into its own slice of a two-slot raw
+// ring, and converts them itself, exactly (every code is a bf16 value),
+// into the bf16 stage layout the score and P . V reads use.  It converts
+// tile t+1 right after its own P . V of tile t-1, whose stage (and kpe
+// slot) tile t+1 reuses: no other wave reads those columns in P . V, and
+// the scores of tile t-1 were done before this iteration's barrier.  So two
+// bf16 stages and two raw slots suffice, with the DMAs still two tiles ahead.
+template <int NW, bool kTileInPage, bool kFp8>
 struct Attn {
   static constexpr int kDimBlocks = (kLoraRank / 32) / NW;  // 32-column blocks of O per wave
-  static constexpr int kLoadsPerWave = kDmaPerTile / NW;    // DMA instructions per tile per wave
+  // DMA instructions per tile per wave: bf16 36 / NW; fp8 16 / NW ckv + 4 / NW kpe.
+  static constexpr int kCkvLoads = kFp8 ? 16 / NW : 0;
+  static constexpr int kKpeLoads = kFp8 ? 4 / NW : 0;
+  static constexpr int kLoadsPerWave = kFp8 ? kCkvLoads + kKpeLoads : kDmaPerTile / NW;
   static_assert(kDmaPerTile % NW == 0 && (kLoraRank / 32) % NW == 0, "NW must be 1, 2 or 4");
   static_assert(kLoadsPerWave <= 63, "vmcnt holds at most 63");
+  static constexpr int kNStages = kFp8 ? 2 : kStages;      // bf16 ckv stages
+  static constexpr int kNKpe = kFp8 ? 2 : kKpeSlots;       // bf16 kpe slots
+  static constexpr int kStageB = kNStages * kCkvBytes;
+  static constexpr int kKpeO = kStageB;
+  // fp8 raw ring: two slots of 18 KiB, wave w's slice at w * kRawWaveBytes
+  // (its ckv instructions at 1 KiB steps, then its kpe ones at 512 B steps).
+  static constexpr int kRawOff = kKpeO + kNKpe * kKpeBytes;
+  static constexpr int kRawSlotBytes = kFp8 ? kLatentDim * kTileKeys : 0;
+  static constexpr int kRawWaveBytes = kRawSlotBytes / NW;
+  static constexpr int kRawSlots = kFp8 ? 2 : 0;
+  static_assert(!kFp8 || kRawWaveBytes == kCkvLoads * 1024 + kKpeLoads * 512, "raw slice");
   static constexpr int kPBufBytes = NW * kPGroupBytes;
-  static constexpr int kPOff = kKpeOff + kKpeSlots * kKpeBytes;  // two P buffers
-  // Per-wave redo flags, in a kpe slot (used after the key loop only).
-  static constexpr int kFlagOff = kKpeOff;
+  static constexpr int kPOff = kRawOff + kRawSlots * kRawSlotBytes;  // two P buffers
+  // Per-wave redo flags (used after the key loop only): in a kpe slot, or
+  // for an fp8 cache in the raw ring (the finish staging reaches into the
+  // kpe slots there).
+  static constexpr int kFlagOff = kFp8 ? kRawOff : kKpeO;
   // Page ids of the current item (tiles that never span pages): an item has
-  // at most kMaxItemTiles tiles, so at most that many pages.
-  static constexpr int kPageOff = kPOff + 2 * kPBufBytes;
+  // at most kMaxItemTiles tiles, so at most that many pages.  Above the
+  // query staging, which is in flight with the page-list DMA.
+  static constexpr int kQWaveBytes = 32 * kLatentDim * 2;
+  static constexpr int kPageOff =
+      kPOff + 2 * kPBufBytes > NW * kQWaveBytes ? kPOff + 2 * kPBufBytes : NW * kQWaveBytes;
   static constexpr int kPageLoads = (kMaxItemTiles + NW * kWave - 1) / (NW * kWave);
   // Tiles that may span pages: each wave keeps the page ids of its lanes'
   // keys for kIdSlots tiles (32 ids of 4 bytes per tile), DMA'd kIdAhead
@@ -175,7 +205,8 @@ struct Attn {
   static constexpr int kFinRow = kDimBlocks * 32 + 4;  // floats (padding staggers banks)
   static constexpr int kFinWaveBytes = 32 * kFinRow * 4;
   static constexpr int kXchgOff = NW * kFinWaveBytes;  // 1/l of every head slot
-  static_assert(kXchgOff + 32 * NW * 4 <= kStageBytes, "finish staging fits the stages");
+  static_assert(kXchgOff + 32 * NW * 4 <= (kFp8 ? kRawOff : kStageB),
+                "finish staging fits the stages (and kpe slots)");
 
   const AttnArgs& a;
   char* smem;
@@ -190,7 +221,8 @@ struct Attn {
   int first_page;  // row page index of the item's first key
 
   __device__ Attn(const AttnArgs& args, char* s) : a(args), smem(s) {
-    scale_log2 = args.scale_log2_ptr ? *args.scale_log2_ptr : args.scale_log2;
+    // (an fp8 cache's scale multiplies every score: out_scale is 1 for bf16)
+    scale_log2 = (args.scale_log2_ptr ? *args.scale_log2_ptr : args.scale_log2) * args.out_scale;
     const int tid = threadIdx.x;
     lane = tid & 63;
     l32 = lane & 31;
@@ -225,10 +257,10 @@ struct Attn {
 
   __device__ __forceinline__ char* pbuf(int t) const { return smem + kPOff + (t & 1) * kPBufBytes; }
   __device__ __forceinline__ const char* stage(int t) const {
-    return smem + (t % kStages) * kCkvBytes;
+    return smem + (t % kNStages) * kCkvBytes;
   }
   __device__ __forceinline__ const char* kpe_slot(int t) const {
-    return smem + kKpeOff + (t % kKpeSlots) * kKpeBytes;
+    return smem + kKpeO + (t % kNKpe) * kKpeBytes;
   }
 
   // Entry i of the item's page list in LDS (as a VGPR value; the caller
@@ -254,6 +286,7 @@ struct Attn {
                  : "m0");
   }
   __device__ __forceinline__ void stage_ids(int t) const {
+    const int lane = opaque(this->lane);  // (address arithmetic made here, per tile)
     if (lane < kTileKeys) {
       const int P = a.page_size;
       const int key = min(kv_begin + t * kTileKeys + lane, kv_end - 1);
@@ -264,6 +297,9 @@ struct Attn {
   // pages at LDS kPageOff + 4 i, by DMA (lanes past the end re-read entry
   // n-1).
   __device__ __forceinline__ void stage_pages(int n) const {
+    // (opaque: the addresses are made per item, not hoisted out of the item
+    // loop into registers the key loop needs)
+    const int lane = opaque(this->lane);
 #pragma unroll
     for (int k = 0; k < kPageLoads; ++k) {
       const int i0 = (k * NW + wave) * kWave;  // this wave's first entry
@@ -285,7 +321,6 @@ struct Attn {
   // load reads full cache lines.  Within a row the 16-byte pieces are
   // permuted (slot c holds piece c ^ (r % 16), q_pe: c ^ (r % 8)) so that
   // the operand reads below, one head per lane, fall in distinct banks.
-  static constexpr int kQWaveBytes = 32 * kLatentDim * 2;
   static_assert(NW * kQWaveBytes <= kPageOff, "the query fits below the page list");
   __device__ __forceinline__ void stage_query(int H) const {
     const char* qn = reinterpret_cast<const char*>(a.q_nope + static_cast<int64_t>(token) * H * kLoraRank);
@@ -365,10 +400,41 @@ struct Attn {
   __device__ __forceinline__ TileDma prep_tile(int t, int pg, int inp) const {
     const int base = kv_begin + t * kTileKeys;
     TileDma d;
+    if constexpr (kFp8) {
+      // Lane l fetches key l%32 (the last key of the item past its end):
+      // ckv chunk pair j is at row offset wave * 512/NW + 16 (l/32) + 32 j,
+      // kpe chunk k (lanes 0..31) at 512 + 16 (kKpeLoads wave + k).
+      d.dst = __builtin_amdgcn_readfirstlane(lds_base + kRawOff + (t % kRawSlots) * kRawSlotBytes +
+                                             wave * kRawWaveBytes);
+      d.dst2 = d.dst;
+      asm volatile("" : "+s"(d.dst));
+      // (opaque: per-tile address arithmetic stays here instead of being
+      // hoisted out of the item loop into registers the key loop needs)
+      const int key = min(opaque(l32), kv_end - 1 - base);
+      const int ckv_off = half * 16 + wave * (kLoraRank / NW);
+      const int kpe_off = kLoraRank + wave * kKpeLoads * 16;
+      if (kTileInPage) {
+        d.sbase = reinterpret_cast<const char*>(
+            a.kv_cache8 + static_cast<int64_t>(pg * a.page_size + inp) * kLatentDim);
+        d.voff_e = static_cast<uint32_t>(key * kLatentDim + ckv_off);
+        d.voff_o = static_cast<uint32_t>(key * kLatentDim + kpe_off);
+        d.src_e = d.src_o = nullptr;
+      } else {
+        const int P = a.page_size;
+        const int pgk = lane_page(t, key);
+        const int r = P == 1 ? pgk : pgk * P + (base + key) % P;
+        const char* row = reinterpret_cast<const char*>(a.kv_cache8 + static_cast<int64_t>(r) * kLatentDim);
+        d.src_e = row + ckv_off;
+        d.src_o = nullptr;  // (kpe addresses are made from src_e when issued)
+        d.sbase = nullptr;
+        d.voff_e = d.voff_o = 0;
+      }
+      return d;
+    }
     // (uniform: pinned to SGPRs here, or the compiler sinks a readfirstlane
     // in front of every DMA)
-    d.dst = __builtin_amdgcn_readfirstlane(lds_base + (t % kStages) * kCkvBytes + wave * 1024);
-    d.dst2 = __builtin_amdgcn_readfirstlane(lds_base + kKpeOff + (t % kKpeSlots) * kKpeBytes +
+    d.dst = __builtin_amdgcn_readfirstlane(lds_base + (t % kNStages) * kCkvBytes + wave * 1024);
+    d.dst2 = __builtin_amdgcn_readfirstlane(lds_base + kKpeO + (t % kNKpe) * kKpeBytes +
                                             wave * 1024 - kCkvBytes);
     asm volatile("" : "+s"(d.dst), "+s"(d.dst2));
     if (kTileInPage) {
@@ -408,6 +474,31 @@ struct Attn {
   // number of waves I has the wave's parity; with one wave, j's.
   template <int j>
   __device__ __forceinline__ void issue_one(const TileDma& d) const {
+    if constexpr (kFp8) {
+      if constexpr (j < kCkvLoads) {  // 1 KiB: two ckv chunks of 32 keys
+        constexpr int kOff = 32 * j;
+        constexpr int kM0 = 1024 * j - kOff;
+        if (kTileInPage)
+          dma16s<kOff, kM0>(d.voff_e, d.sbase, d.dst);
+        else
+          dma16<kOff, kM0>(d.src_e, d.dst);
+      } else {  // 512 B, lanes 0..31: one kpe chunk of 32 keys
+        constexpr int k = j - kCkvLoads;
+        constexpr int kOff = 16 * k;
+        constexpr int kM0 = 1024 * kCkvLoads + 512 * k - kOff;
+        if (lane < 32) {
+          if (kTileInPage) {
+            dma16s<kOff, kM0>(d.voff_o, d.sbase, d.dst);
+          } else {
+            // lanes 0..31 (first half): from this wave's ckv offset to its kpe one
+            const int delta = __builtin_amdgcn_readfirstlane(kLoraRank + wave * kKpeLoads * 16 -
+                                                             wave * (kLoraRank / NW));
+            dma16<kOff, kM0>(d.src_e + delta, d.dst);
+          }
+        }
+      }
+      return;
+    }
     constexpr int kOff = j * NW * 32;
     // The instruction offset moves the LDS destination as well as the
     // global address, so M0 takes it back off.
@@ -425,6 +516,55 @@ struct Attn {
     if constexpr (j0 < j1) {
       issue_one<j0>(d);
       issue_range<j0 + 1, j1>(d);
+    }
+  }
+
+  // fp8 cache: this wave's codes of tile t (its raw slice) converted to
+  // bf16 into stage t and kpe slot t, at the places the score and P . V
+  // reads expect (16-column chunk c of key k becomes the 8-column chunks
+  // 2c and 2c+1).  Exact: every E4M3 value is a bf16 value.
+  __device__ __forceinline__ void convert_tile(int t) const {
+    const char* raw = smem + kRawOff + (t % kRawSlots) * kRawSlotBytes + wave * kRawWaveBytes +
+                      lane * 16;
+    char* stg = smem + (t % kNStages) * kCkvBytes;
+    char* kp = smem + kKpeO + (t % kNKpe) * kKpeBytes;
+    auto cvt = [](uint32_t w0, uint32_t w1) {
+      u32x4_t o;
+      o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+      o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+      o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+      o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+      return o;
+    };
+    // (two chunks in flight: the scheduler may not hoist every read, the
+    // key loop's registers are nearly all taken)
+    constexpr int kAhead = 2;
+    u32x4_t r[kAhead];
+#pragma unroll
+    for (int j = 0; j < kAhead && j < kCkvLoads; ++j)
+      r[j] = *reinterpret_cast<const u32x4_t*>(raw + j * 1024);
+    static_for<kCkvLoads>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const u32x4_t cur = r[j % kAhead];
+      if constexpr (j + kAhead < kCkvLoads)
+        r[j % kAhead] = *reinterpret_cast<const u32x4_t*>(raw + (j + kAhead) * 1024);
+      const int c = (32 / NW) * wave + 2 * j + half;  // 16-column chunk of the key
+      const int sw = kSwzB * (c & 1);
+      char* dst = stg + c * 1024;
+      *reinterpret_cast<u32x4_t*>(dst + ((l32 ^ sw) * 16)) = cvt(cur[0], cur[1]);
+      *reinterpret_cast<u32x4_t*>(dst + 512 + ((l32 ^ kSwzA ^ sw) * 16)) = cvt(cur[2], cur[3]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if (lane < 32) {
+#pragma unroll
+      for (int k = 0; k < kKpeLoads; ++k) {
+        const u32x4_t q = *reinterpret_cast<const u32x4_t*>(raw + kCkvLoads * 1024 + k * 512);
+        const int kc = kKpeLoads * wave + k;  // kpe 16-column chunk
+        const int sw = kSwzB * (kc & 1);
+        char* dst = kp + kc * 1024;
+        *reinterpret_cast<u32x4_t*>(dst + ((l32 ^ sw) * 16)) = cvt(q[0], q[1]);
+        *reinterpret_cast<u32x4_t*>(dst + 512 + ((l32 ^ kSwzA ^ sw) * 16)) = cvt(q[2], q[3]);
+      }
     }
   }
 
@@ -558,6 +698,11 @@ struct Attn {
           }
         // The next tile's page id, read a tile ahead.
         int pg_next = kTileInPage ? page_at(min(cur_pl, n_pages - 1)) : 0;
+        if constexpr (kFp8) {
+          // This wave's codes of tile 0 (tile 1's may still be in flight).
+          wait_vm(ntiles > 1, false);
+          convert_tile(0);
+        }
         // Tile t: S(t), with the DMAs of tile t+2 between its k-steps; the
         // softmax of S(t); P(t) published in LDS; this wave's columns of
         // P(t) . V(t) for every head.  With several waves the tiles are
@@ -571,7 +716,7 @@ struct Attn {
         for (int t = 0; t < ntiles; ++t) {
           // (iteration t-1 staged the ids of tile t-1+kIdAhead, if any; the
           // prologue stages none after its tiles)
-          wait_vm(t + 1 < ntiles, !kTileInPage && t > 0 && t + kIdAhead - 1 < ntiles);
+          if (!kFp8) wait_vm(t + 1 < ntiles, !kTileInPage && t > 0 && t + kIdAhead - 1 < ntiles);
           lds_barrier();
           const bool dma = t + kTilesAhead < ntiles;
           const int base = kv_begin + t * kTileKeys;
@@ -629,6 +774,17 @@ struct Attn {
             lds_barrier();
             pv(stage(t), pbuf(t), o, [&](auto) {});
           }
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (kFp8) {
+            // Tile t+1 into the stage of tile t-1, whose columns of this wave
+            // P . V has just finished with.  Its codes were DMA'd an
+            // iteration ago; tile t+2's (and a page-id DMA issued before
+            // them) may still be in flight.
+            if (t + 1 < ntiles) {
+              wait_vm(dma, !kTileInPage && t + kIdAhead < ntiles);
+              convert_tile(t + 1);
+            }
+          }
         }
         if (kPipe) {
           lds_barrier();
@@ -652,7 +808,7 @@ struct Attn {
     // tell the host this workgroup is done with the slot.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
-    if (a.done_flags && threadIdx.x == 0)
+    if (a.done_flags && wave == 0 && lane == 0)
       __hip_atomic_store(a.done_flags + blockIdx.x, a.run_seq, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_SYSTEM);
   }
@@ -814,7 +970,7 @@ struct Attn {
     const bool head_ok = head < a.num_heads;
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const bool any = l_tot > 0.f;
-    const float inv = any ? 1.f / l_tot : 0.f;
+    const float inv = any ? a.out_scale / l_tot : 0.f;
     const float lse_v = any ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
     const int H = a.num_heads;
     // A final item writes the token's output and LSE; a piece of a split
@@ -886,23 +1042,30 @@ struct Attn {
   }
 };
 
-template <int NW, bool kTileInPage>
+template <int NW, bool kTileInPage, bool kFp8>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attention_kernel(AttnArgs args) {
-  __shared__ __attribute__((aligned(1024))) char smem[Attn<NW, kTileInPage>::kLdsBytes];
-  Attn<NW, kTileInPage> k(args, smem);
+  __shared__ __attribute__((aligned(1024))) char smem[Attn<NW, kTileInPage, kFp8>::kLdsBytes];
+  Attn<NW, kTileInPage, kFp8> k(args, smem);
   k.run();
 }
 
-template <int NW>
+template <int NW, bool kFp8>
 hipError_t launch_nw(const AttnArgs& a, int num_workers, hipStream_t stream) {
   if (a.page_size % kTileKeys == 0)
-    hipLaunchKernelGGL((attention_kernel<NW, true>), dim3(num_workers), dim3(NW * kWave), 0,
+    hipLaunchKernelGGL((attention_kernel<NW, true, kFp8>), dim3(num_workers), dim3(NW * kWave), 0,
                        stream, a);
   else
-    hipLaunchKernelGGL((attention_kernel<NW, false>), dim3(num_workers), dim3(NW * kWave), 0,
-                       stream, a);
+    hipLaunchKernelGGL((attention_kernel<NW, false, kFp8>), dim3(num_workers), dim3(NW * kWave),
+                       0, stream, a);
   return hipGetLastError();
+}
+
+template <bool kFp8>
+hipError_t launch_dtype(const AttnArgs& a, int num_workers, hipStream_t stream) {
+  if (a.num_heads <= 32) return launch_nw<1, kFp8>(a, num_workers, stream);
+  if (a.num_heads <= 64) return launch_nw<2, kFp8>(a, num_workers, stream);
+  return launch_nw<4, kFp8>(a, num_workers, stream);
 }
 
 }  // namespace
@@ -910,9 +1073,8 @@ hipError_t launch_nw(const AttnArgs& a, int num_workers, hipStream_t stream) {
 hipError_t launch_attention(const AttnArgs& a, int num_workers, hipStream_t stream) {
   if (num_workers <= 0) return hipSuccess;
   if (a.num_heads <= 0 || a.num_heads > kMaxHeads) return hipErrorInvalidValue;
-  if (a.num_heads <= 32) return launch_nw<1>(a, num_workers, stream);
-  if (a.num_heads <= 64) return launch_nw<2>(a, num_workers, stream);
-  return launch_nw<4>(a, num_workers, stream);
+  return a.kv_cache8 ? launch_dtype<true>(a, num_workers, stream)
+                     : launch_dtype<false>(a, num_workers, stream);
 }
 
 }  // namespace mla

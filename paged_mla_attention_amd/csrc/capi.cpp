@@ -484,15 +484,22 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
   return MLA_OK;
 }
 
-mla_status mla_run(mla_plan_t p, const void* q_nope, const void* q_pe, const void* kv_cache,
-                   void* out, float* lse, mla_stream_t stream_) {
+}  // extern "C"
+
+namespace {
+
+// mla_run / mla_run_fp8: kv_cache8 set selects the fp8 cache, whose scale
+// multiplies the softmax scale and the normalised output.
+mla_status run_impl(mla_plan_t p, const void* q_nope, const void* q_pe, const void* kv_cache,
+                    const void* kv_cache8, float kv_scale, void* out, float* lse,
+                    mla_stream_t stream_) {
   mla::clear_last_error();
   if (!p) return fail(MLA_E_INVALID, "NULL plan");
   if (!p->planned) return fail(MLA_E_STATE, "mla_run before a successful mla_plan");
   const auto& s = p->sched;
   if (s.num_tokens == 0) return MLA_OK;
   if (!q_nope || !q_pe || !out) return fail(MLA_E_INVALID, "NULL q_nope, q_pe or out");
-  if (!kv_cache && s.nnz > 0) return fail(MLA_E_INVALID, "NULL kv_cache");
+  if (!kv_cache && !kv_cache8 && s.nnz > 0) return fail(MLA_E_INVALID, "NULL kv_cache");
   DeviceGuard g(p->device);
   if (g.err != hipSuccess) return hip_fail(g.err, "hipSetDevice");
   hipStream_t stream = static_cast<hipStream_t>(stream_);
@@ -504,6 +511,7 @@ mla_status mla_run(mla_plan_t p, const void* q_nope, const void* q_pe, const voi
   a.q_nope = static_cast<const uint16_t*>(q_nope);
   a.q_pe = static_cast<const uint16_t*>(q_pe);
   a.kv_cache = static_cast<const uint16_t*>(kv_cache);
+  a.kv_cache8 = static_cast<const uint8_t*>(kv_cache8);
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
   a.part_o = reinterpret_cast<uint16_t*>(p->d_part);
@@ -518,6 +526,7 @@ mla_status mla_run(mla_plan_t p, const void* q_nope, const void* q_pe, const voi
   a.num_heads = p->num_heads;
   a.page_size = p->page_size;
   a.scale_log2 = p->scale_log2;
+  a.out_scale = kv_cache8 ? kv_scale : 1.f;
   // A schedule read from the host slot: the attention workgroups report when
   // they are done with it (no event between the kernels; runs of one plan
   // are stream-ordered, so a slot's flags only grow), and the merge list
@@ -567,8 +576,31 @@ mla_status mla_run(mla_plan_t p, const void* q_nope, const void* q_pe, const voi
   return MLA_OK;
 }
 
-mla_status mla_append_kv(mla_plan_t p, const void* ckv, const void* kpe, void* kv_cache,
-                         mla_stream_t stream_) {
+}  // namespace
+
+extern "C" {
+
+mla_status mla_run(mla_plan_t p, const void* q_nope, const void* q_pe, const void* kv_cache,
+                   void* out, float* lse, mla_stream_t stream) {
+  return run_impl(p, q_nope, q_pe, kv_cache, nullptr, 1.f, out, lse, stream);
+}
+
+mla_status mla_run_fp8(mla_plan_t p, const void* q_nope, const void* q_pe,
+                       const void* kv_cache_fp8, float kv_scale, void* out, float* lse,
+                       mla_stream_t stream) {
+  if (!(std::isfinite(kv_scale) && kv_scale > 0.f)) {
+    mla::clear_last_error();
+    return fail(MLA_E_INVALID, "kv_scale must be finite and positive");
+  }
+  return run_impl(p, q_nope, q_pe, nullptr, kv_cache_fp8, kv_scale, out, lse, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+mla_status append_impl(mla_plan_t p, const void* ckv, const void* kpe, void* kv_cache, bool fp8,
+                       float kv_scale, mla_stream_t stream_) {
   mla::clear_last_error();
   if (!p) return fail(MLA_E_INVALID, "NULL plan");
   if (!p->planned) return fail(MLA_E_STATE, "mla_append_kv before a successful mla_plan");
@@ -594,9 +626,14 @@ mla_status mla_append_kv(mla_plan_t p, const void* ckv, const void* kpe, void* k
     std::memcpy(rows.inline_rows, s.append_rows.data(), s.append_rows.size() * sizeof(int32_t));
   else
     rows.rows = reinterpret_cast<const int32_t*>(d + p->off_append);
-  hipError_t e = mla::launch_append_kv(static_cast<const uint16_t*>(ckv),
-                                       static_cast<const uint16_t*>(kpe), rows,
-                                       static_cast<uint16_t*>(kv_cache), s.num_tokens, stream);
+  hipError_t e =
+      fp8 ? mla::launch_append_kv_fp8(static_cast<const uint16_t*>(ckv),
+                                      static_cast<const uint16_t*>(kpe), rows,
+                                      static_cast<uint8_t*>(kv_cache), kv_scale, s.num_tokens,
+                                      stream)
+          : mla::launch_append_kv(static_cast<const uint16_t*>(ckv),
+                                  static_cast<const uint16_t*>(kpe), rows,
+                                  static_cast<uint16_t*>(kv_cache), s.num_tokens, stream);
   if (e != hipSuccess) return hip_fail(e, "append launch");
   if (p->direct && !inline_rows) {
     // The kernel reads the host slot (as mla_run does).
@@ -610,6 +647,24 @@ mla_status mla_append_kv(mla_plan_t p, const void* ckv, const void* kpe, void* k
     }
   }
   return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_append_kv(mla_plan_t p, const void* ckv, const void* kpe, void* kv_cache,
+                         mla_stream_t stream) {
+  return append_impl(p, ckv, kpe, kv_cache, false, 1.f, stream);
+}
+
+mla_status mla_append_kv_fp8(mla_plan_t p, const void* ckv, const void* kpe, void* kv_cache_fp8,
+                             float kv_scale, mla_stream_t stream) {
+  if (!(std::isfinite(kv_scale) && kv_scale > 0.f)) {
+    mla::clear_last_error();
+    return fail(MLA_E_INVALID, "kv_scale must be finite and positive");
+  }
+  return append_impl(p, ckv, kpe, kv_cache_fp8, true, kv_scale, stream);
 }
 
 static mla_status projection(hipError_t (*launch)(const uint16_t*, const uint16_t*, uint16_t*,

@@ -12,7 +12,8 @@ namespace mla {
 struct AttnArgs {
   const uint16_t* q_nope;    // bf16 [T, H, 512]
   const uint16_t* q_pe;      // bf16 [T, H, 64]
-  const uint16_t* kv_cache;  // bf16 [pages, page_size, 576]
+  const uint16_t* kv_cache;  // bf16 [pages, page_size, 576] (bf16 cache)
+  const uint8_t* kv_cache8;  // fp8 e4m3 codes [pages, page_size, 576] (fp8 cache)
   uint16_t* out;             // bf16 [T, H, 512]
   float* lse;                // fp32 [T, H] or nullptr
   uint16_t* part_o;          // bf16 [slots, H, 512], normalised output of each piece
@@ -24,6 +25,10 @@ struct AttnArgs {
   int32_t num_heads;
   int32_t page_size;
   float scale_log2;  // sm_scale * log2(e)
+  // 1 for a bf16 cache; kv_scale for an fp8 cache, whose codes the kernel
+  // reads unscaled: it multiplies the scores (with scale_log2) and the
+  // normalised output.
+  float out_scale;
   const float* scale_log2_ptr;  // non-null: read the scale here (reserved plans)
   // Schedule read from a pinned host slot: each workgroup stores run_seq to
   // done_flags[workgroup] once it has read the slot for the last time (the
@@ -65,7 +70,9 @@ struct SplitMergeArgs {
   const int32_t* num_merges_ptr;  // non-null: the live count, <= num_merges (reserved plans)
 };
 
-// Attention over every planned work item: one workgroup per worker.
+// Attention over every planned work item: one workgroup per worker.  An
+// fp8 cache (a.kv_cache8 set) is read as E4M3 codes whose values the
+// arguments' scale factors carry.
 hipError_t launch_attention(const AttnArgs& a, int num_workers, hipStream_t stream);
 
 // Combines the partial results of tokens whose keys were split.
@@ -74,6 +81,11 @@ hipError_t launch_split_merge(const SplitMergeArgs& a, hipStream_t stream);
 // KV append: latent row of token t ([ckv[t] | kpe[t]]) to cache row rows[t].
 hipError_t launch_append_kv(const uint16_t* ckv, const uint16_t* kpe, const AppendRows& rows,
                             uint16_t* cache, int64_t num_tokens, hipStream_t stream);
+// The same into an fp8 cache: each value stored as the E4M3 code nearest to
+// fp32(x / kv_scale) (ties to even, saturated at +-448).
+hipError_t launch_append_kv_fp8(const uint16_t* ckv, const uint16_t* kpe, const AppendRows& rows,
+                                uint8_t* cache, float kv_scale, int64_t num_tokens,
+                                hipStream_t stream);
 
 // Per-head projections: out[t, h, :] = x[t, h, :] @ w[h] (bf16, fp32
 // accumulation).  Absorption: [T, H, 128] x [H, 128, 512]; up-projection:

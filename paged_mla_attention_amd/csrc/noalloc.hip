@@ -448,6 +448,7 @@ extern "C" mla_status mla_run_noalloc(const int32_t* qo_indptr, const int32_t* k
   a.num_heads = num_heads;
   a.page_size = page_size;
   a.scale_log2 = sm_scale * 1.44269504088896340736f;
+  a.out_scale = 1.f;
   e = launch_attention(a, W, stream);
   if (e != hipSuccess) return na_fail(MLA_E_HIP, hipGetErrorString(e));
 

@@ -1,0 +1,166 @@
+"""fp8 (E4M3) latent cache on the GPU, through the C ABI (mla_run_fp8,
+mla_append_kv_fp8), against the fp64 oracle: ragged batches over every
+kernel variant (one, two and four waves; tiles inside pages and per-key
+pages), the full decode and long-decode batches, the overflow-redo path,
+and the quantising append bit for bit."""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import assert_close, from_dev_bf16
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_mla_attention_amd as pm
+    pm.library()
+
+
+def _dev_bits(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _run_fp8(w, codes, scale, plan=None):
+    import paged_mla_attention_amd as pm
+    own = plan is None
+    if own:
+        plan = pm.MLAPlan(w.num_heads, w.page_size)
+    plan.plan(w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_len, causal=w.causal,
+              sm_scale=w.sm_scale, num_cache_pages=w.num_pages, kv_dtype="fp8_e4m3")
+    kv = torch.from_numpy(np.ascontiguousarray(codes)).cuda()
+    o, lse = plan.run(_dev_bits(w.q_nope), _dev_bits(w.q_pe), kv, return_lse=True, kv_scale=scale)
+    torch.cuda.synchronize()
+    if own:
+        plan.close()
+    return from_dev_bf16(o), lse.cpu().numpy()
+
+
+def _oracle_fp8(w, codes, scale, tokens=None):
+    return oracle.attention_fp8(w.q_nope, w.q_pe, codes, w.qo_indptr, w.kv_indptr, w.kv_indices,
+                                w.kv_last_page_len, w.page_size, w.causal, w.sm_scale, scale,
+                                tokens=tokens)
+
+
+@pytest.mark.parametrize("heads", [16, 32, 64, 128])
+@pytest.mark.parametrize("page_size", [1, 16, 33, 64])
+def test_fp8_ragged_small(heads, page_size):
+    rng = np.random.default_rng(300 + heads + page_size)
+    w = W.make_workload("fp8_ragged", 0, [1, 95, 0, 300, 64, 7], [1, 3, 2, 40, 1, 9], heads,
+                        page_size, rng=rng)
+    scale = 0.37 if heads % 32 == 0 else 1 / 16
+    codes = W.fp8_cache_codes(w.kv_cache, scale)
+    o, lse = _run_fp8(w, codes, scale)
+    o_ref, l_ref = _oracle_fp8(w, codes, scale)
+    assert_close(o, lse, o_ref, l_ref, f"fp8 ragged H={heads} P={page_size}")
+
+
+def test_fp8_decode_b64_h128_full():
+    w = W.decode_batch()
+    scale = 1 / 32
+    codes = W.fp8_cache_codes(w.kv_cache, scale)
+    o, lse = _run_fp8(w, codes, scale)
+    o_ref, l_ref = _oracle_fp8(w, codes, scale)
+    assert_close(o, lse, o_ref, l_ref, "fp8 decode B=64 H=128")
+
+
+def test_fp8_long_decode_full():
+    w = W.long_decode()
+    scale = 0.05
+    codes = W.fp8_cache_codes(w.kv_cache, scale)
+    o, lse = _run_fp8(w, codes, scale)
+    o_ref, l_ref = _oracle_fp8(w, codes, scale)
+    assert_close(o, lse, o_ref, l_ref, "fp8 long decode")
+
+
+@pytest.mark.parametrize("heads", [32, 128])
+@pytest.mark.parametrize("page_size", [32, 33])
+def test_fp8_extreme_score_range_redo(heads, page_size):
+    """Scores jumping by far more than 2^64 after an item's first tile (the
+    redo path) over an fp8 cache."""
+    rng = np.random.default_rng(41 + heads + page_size)
+    kv, qo = [256, 300], [1, 24]
+    w = W.make_workload("fp8_extreme", 0, kv, qo, heads, page_size, rng=rng)
+    qscale = 1.0 + np.arange(heads) / heads
+    w.q_nope[:] = W.f32_to_bf16_bits(np.broadcast_to(
+        qscale[None, :, None], (w.num_tokens, heads, 512)).astype(np.float32))
+    w.q_pe[:] = 0
+    for b, L in enumerate(kv):
+        c = np.where(np.arange(L) < 32, 0.01, np.where(np.arange(L) < 40, 0.5, 3.0))
+        for j in range(L):
+            pg = w.kv_indices[w.kv_indptr[b] + j // page_size]
+            w.kv_cache[pg, j % page_size, :512] = W.f32_to_bf16_bits(np.full(512, c[j], np.float32))
+    scale = 1 / 64
+    codes = W.fp8_cache_codes(w.kv_cache, scale)
+    o, lse = _run_fp8(w, codes, scale)
+    o_ref, l_ref = _oracle_fp8(w, codes, scale)
+    assert_close(o, lse, o_ref, l_ref, f"fp8 extreme H={heads} P={page_size}")
+
+
+@pytest.mark.parametrize("page_size", [1, 16, 64])
+def test_fp8_append_bit_exact(page_size):
+    """The quantising append writes the oracle's codes, byte for byte, and
+    leaves every other byte of the cache alone."""
+    import paged_mla_attention_amd as pm
+    rng = np.random.default_rng(60 + page_size)
+    w = W.make_workload("fp8_append", 0, [40, 3, 700, 129], [2, 3, 1, 64], 16, page_size, rng=rng)
+    scale = 0.3
+    codes = W.fp8_cache_codes(w.kv_cache, scale)
+    T = w.num_tokens
+    ckv = W.bf16_normals(rng, (T, 512))
+    kpe = W.bf16_normals(rng, (T, 64))
+    ckv[0, :8] = W.f32_to_bf16_bits(np.array([1000, -1000, 1e-30, -1e-30, 0, 134.4, 67.2, -0.0],
+                                             np.float32))
+    plan = pm.MLAPlan(16, page_size)
+    plan.plan(w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_len,
+              num_cache_pages=w.num_pages, kv_dtype="fp8_e4m3")
+    kv = torch.from_numpy(codes.copy()).cuda()
+    plan.append_kv(_dev_bits(ckv), _dev_bits(kpe), kv, kv_scale=scale)
+    torch.cuda.synchronize()
+    plan.close()
+    want = oracle.append_kv_fp8(codes, ckv, kpe, w.qo_indptr, w.kv_indptr, w.kv_indices,
+                                w.kv_last_page_len, page_size, scale)
+    got = kv.cpu().numpy()
+    assert np.array_equal(got, want), f"{int((got != want).sum())} bytes differ"
+
+
+def test_fp8_append_then_attend_decode():
+    """Decode batch: append each row's new token into the fp8 cache, then
+    attend; the result matches the oracle's append + attention."""
+    import paged_mla_attention_amd as pm
+    w = W.decode_batch()
+    scale = 1 / 32
+    codes = W.fp8_cache_codes(w.kv_cache, scale)
+    rng = np.random.default_rng(77)
+    ckv, kpe = W.bf16_normals(rng, (64, 512)), W.bf16_normals(rng, (64, 64))
+    plan = pm.MLAPlan(128, 64)
+    plan.plan(w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_len,
+              num_cache_pages=w.num_pages, kv_dtype="fp8_e4m3")
+    kv = torch.from_numpy(codes.copy()).cuda()
+    plan.append_kv(_dev_bits(ckv), _dev_bits(kpe), kv, kv_scale=scale)
+    o, lse = plan.run(_dev_bits(w.q_nope), _dev_bits(w.q_pe), kv, return_lse=True,
+                      kv_scale=scale)
+    torch.cuda.synchronize()
+    plan.close()
+    want = oracle.append_kv_fp8(codes, ckv, kpe, w.qo_indptr, w.kv_indptr, w.kv_indices,
+                                w.kv_last_page_len, 64, scale)
+    assert np.array_equal(kv.cpu().numpy(), want)
+    o_ref, l_ref = _oracle_fp8(w, want, scale)
+    assert_close(from_dev_bf16(o), lse.cpu().numpy(), o_ref, l_ref, "fp8 append + decode")
+
+
+def test_fp8_rejects_bad_scale():
+    import paged_mla_attention_amd as pm
+    from paged_mla_attention_amd import _native
+    w = W.tiny()
+    codes = W.fp8_cache_codes(w.kv_cache, 1.0)
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        with pytest.raises(_native.MLAError, match="kv_scale"):
+            _run_fp8(w, codes, bad)

@@ -245,3 +245,13 @@ WORKLOADS = {
     "prefill": chunked_prefill,
     "mixed": mixed,
 }
+
+
+def fp8_cache_codes(kv_cache_bits: np.ndarray, kv_scale: float) -> np.ndarray:
+    """An fp8 (E4M3) latent cache standing for a bf16 one: the bf16 values
+    divided by kv_scale, clamped to +-448 and converted by PyTorch's
+    float8_e4m3fn rounding; returns the codes (uint8), same shape."""
+    import torch
+    f = (np.ascontiguousarray(kv_cache_bits).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    t = torch.from_numpy(f / np.float32(kv_scale)).clamp(-448.0, 448.0)
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
