@@ -43,11 +43,12 @@ ROW_BYTES = 576 * 2
 FLOPS_PER_PAIR = 2 * 576 + 2 * 512
 
 
-def algorithmic(w, return_lse=True):
-    """Bytes and flops the method must move/compute for workload w."""
+def algorithmic(w, return_lse=True, row_bytes=ROW_BYTES):
+    """Bytes and flops the method must move/compute for workload w (a latent
+    row is 1152 bytes in a bf16 cache, 576 in an fp8 one)."""
     lens = w.kv_lens()
     T, H = w.num_tokens, w.num_heads
-    nbytes = ROW_BYTES * int(lens.sum()) + T * H * (576 * 2 + 512 * 2)
+    nbytes = row_bytes * int(lens.sum()) + T * H * (576 * 2 + 512 * 2)
     if return_lse:
         nbytes += 4 * T * H
     nbytes += 4 * (2 * (w.batch + 1) + w.batch + int(w.kv_indptr[-1]))
@@ -91,12 +92,15 @@ def _to_dev_bf16(bits, torch):
     return t.view(torch.bfloat16).cuda()
 
 
-def run_steps(w, steps, warmup, copies=3):
+def run_steps(w, steps, warmup, copies=3, fp8_scale=None):
     import torch
 
     import paged_mla_attention_amd as pm
     T, H = w.num_tokens, w.num_heads
-    kv0 = _to_dev_bf16(w.kv_cache, torch)
+    if fp8_scale is None:
+        kv0 = _to_dev_bf16(w.kv_cache, torch)
+    else:  # an fp8 (E4M3) cache standing for the bf16 one
+        kv0 = torch.from_numpy(W.fp8_cache_codes(w.kv_cache, fp8_scale)).cuda()
     qn0, qp0 = _to_dev_bf16(w.q_nope, torch), _to_dev_bf16(w.q_pe, torch)
     kvs = [kv0] + [kv0.clone() for _ in range(copies - 1)]
     qns = [qn0] + [qn0.clone() for _ in range(copies - 1)]
@@ -107,9 +111,11 @@ def run_steps(w, steps, warmup, copies=3):
     qo, kvp, idx, last = (np.ascontiguousarray(a, dtype=np.int32) for a in
                           (w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_len))
 
+    kv_dtype = None if fp8_scale is None else "fp8_e4m3"
+
     def do_plan():
         plan.plan(qo, kvp, idx, last, causal=w.causal, sm_scale=w.sm_scale,
-                  num_cache_pages=w.num_pages)
+                  num_cache_pages=w.num_pages, kv_dtype=kv_dtype)
 
     # A step is one plan and one run.  As in a serving loop, the plan of the
     # next step is made while this step's kernels run.  One pair of events on
@@ -117,7 +123,7 @@ def run_steps(w, steps, warmup, copies=3):
     # would put their own markers between the kernels).
     def step(k):
         c = k % copies
-        plan.run(qns[c], qps[c], kvs[c], out=outs[c], lse=lses[c])
+        plan.run(qns[c], qps[c], kvs[c], out=outs[c], lse=lses[c], kv_scale=fp8_scale)
         do_plan()
 
     do_plan()
@@ -150,7 +156,7 @@ def run_steps(w, steps, warmup, copies=3):
     for k in range(20):
         t1 = time.perf_counter()
         plan.plan(qo, kvp, idx2 if k % 2 == 0 else idx, last, causal=w.causal,
-                  sm_scale=w.sm_scale, num_cache_pages=w.num_pages)
+                  sm_scale=w.sm_scale, num_cache_pages=w.num_pages, kv_dtype=kv_dtype)
         full.append(time.perf_counter() - t1)
     torch.cuda.synchronize()
     stats["full_plan_host_us"] = round(float(np.median(full)) * 1e6, 1)
@@ -182,6 +188,18 @@ def other_workloads(steps):
     _, run_ms, stats = run_steps(wl, steps, 50, copies=1)
     out["long_decode"] = dict(roofline_entry(wl, run_ms, b, f), plan=stats)
     print(f"[bench] long decode: mla_run {run_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+
+    # fp8 (E4M3) caches: GB/s on the fp8 bytes (576 per latent row)
+    wd = W.decode_batch()
+    b, f = algorithmic(wd, row_bytes=576)
+    _, run_ms, _ = run_steps(wd, steps, 50, fp8_scale=1 / 32)
+    out["decode_fp8"] = roofline_entry(wd, run_ms, b, f)
+    out["decode_fp8"]["workload"] = wd.name + "_fp8"
+    b, f = algorithmic(wl, row_bytes=576)
+    _, run_ms, _ = run_steps(wl, steps, 50, copies=1, fp8_scale=0.05)
+    out["long_decode_fp8"] = roofline_entry(wl, run_ms, b, f)
+    out["long_decode_fp8"]["workload"] = wl.name + "_fp8"
+    print(f"[bench] fp8 decode and long decode done", file=sys.stderr, flush=True)
 
     wm = W.mixed()
     b, f = algorithmic(wm)

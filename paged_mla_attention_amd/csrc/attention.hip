@@ -160,8 +160,14 @@ __device__ __forceinline__ int opaque(int v) {
 // slot) tile t+1 reuses: no other wave reads those columns in P . V, and
 // the scores of tile t-1 were done before this iteration's barrier.  So two
 // bf16 stages and two raw slots suffice, with the DMAs still two tiles ahead.
-template <int NW, bool kTileInPage, bool kFp8>
+// A compact one-wave variant (kCompact, bf16 cache): two ckv stages and two
+// kpe slots with one tile in flight, 80 KiB of LDS, so that two workgroups
+// share a compute unit (the host plans two workers per compute unit for it).
+template <int NW, bool kTileInPage, bool kFp8, bool kCompact>
 struct Attn {
+  static_assert(!kCompact || (NW == 1 && !kFp8), "the compact variant is one wave, bf16");
+  // Tiles whose DMAs are in flight beyond the one being computed.
+  static constexpr int kAhead = kCompact ? 1 : kTilesAhead;
   static constexpr int kDimBlocks = (kLoraRank / 32) / NW;  // 32-column blocks of O per wave
   // DMA instructions per tile per wave: bf16 36 / NW; fp8 16 / NW ckv + 4 / NW kpe.
   static constexpr int kCkvLoads = kFp8 ? 16 / NW : 0;
@@ -169,8 +175,8 @@ struct Attn {
   static constexpr int kLoadsPerWave = kFp8 ? kCkvLoads + kKpeLoads : kDmaPerTile / NW;
   static_assert(kDmaPerTile % NW == 0 && (kLoraRank / 32) % NW == 0, "NW must be 1, 2 or 4");
   static_assert(kLoadsPerWave <= 63, "vmcnt holds at most 63");
-  static constexpr int kNStages = kFp8 ? 2 : kStages;      // bf16 ckv stages
-  static constexpr int kNKpe = kFp8 ? 2 : kKpeSlots;       // bf16 kpe slots
+  static constexpr int kNStages = kFp8 || kCompact ? 2 : kStages;  // bf16 ckv stages
+  static constexpr int kNKpe = kFp8 || kCompact ? 2 : kKpeSlots;     // bf16 kpe slots
   static constexpr int kStageB = kNStages * kCkvBytes;
   static constexpr int kKpeO = kStageB;
   // fp8 raw ring: two slots of 18 KiB, wave w's slice at w * kRawWaveBytes
@@ -205,7 +211,8 @@ struct Attn {
   static constexpr int kFinRow = kDimBlocks * 32 + 4;  // floats (padding staggers banks)
   static constexpr int kFinWaveBytes = 32 * kFinRow * 4;
   static constexpr int kXchgOff = NW * kFinWaveBytes;  // 1/l of every head slot
-  static_assert(kXchgOff + 32 * NW * 4 <= (kFp8 ? kRawOff : kStageB),
+  // (a lone wave reads its redo flags before its finish staging covers them)
+  static_assert(kXchgOff + 32 * NW * 4 <= (kFp8 ? kRawOff : (kCompact ? kPOff : kStageB)),
                 "finish staging fits the stages (and kpe slots)");
 
   const AttnArgs& a;
@@ -389,7 +396,7 @@ struct Attn {
     const char* src_o;  //   even / odd I (+ 32 wave)
     const char* sbase;  // tile in one page: page base (uniform) ...
     uint32_t voff_e;    // ... and the lane row offsets for even / odd I
-    uint32_t voff_o;
+    uint32_t voff_o;    //   (several waves: voff_e is this wave's, of its parity)
     uint32_t dst;       // LDS address of DMA I = wave (ckv stage) ...
     uint32_t dst2;      // ... and of I = wave + 32 (kpe slot), less 32 KiB
   };
@@ -442,8 +449,13 @@ struct Attn {
       const int lane_c = ld_off + wave * 32;
       d.sbase = reinterpret_cast<const char*>(
           a.kv_cache + static_cast<int64_t>(pg * a.page_size + inp) * kLatentDim);
-      d.voff_e = static_cast<uint32_t>(min(ld_key, rem) * (kLatentDim * 2) + lane_c);
-      d.voff_o = static_cast<uint32_t>(min(ld_key ^ kSwzB, rem) * (kLatentDim * 2) + lane_c);
+      // With several waves each wave loads one of the two key orders only
+      // (selected here, once per tile: a select in front of each DMA puts
+      // a VALU result on the DMA's address path).
+      const int key_e = NW == 1 || (wave & 1) == 0 ? ld_key : (ld_key ^ kSwzB);
+      d.voff_e = static_cast<uint32_t>(min(key_e, rem) * (kLatentDim * 2) + lane_c);
+      d.voff_o = NW == 1 ? static_cast<uint32_t>(min(ld_key ^ kSwzB, rem) * (kLatentDim * 2) + lane_c)
+                         : d.voff_e;
       d.src_e = d.src_o = nullptr;
     } else {
       const int P = a.page_size;
@@ -504,9 +516,8 @@ struct Attn {
     // global address, so M0 takes it back off.
     constexpr int kM0 = j * NW * 1024 - kOff;
     const uint32_t dbase = j * NW < kCkvDmas ? d.dst : d.dst2;
-    const bool odd = NW == 1 ? (j & 1) : (wave & 1);
     if (kTileInPage)
-      dma16s<kOff, kM0>(odd ? d.voff_o : d.voff_e, d.sbase, dbase);
+      dma16s<kOff, kM0>(NW == 1 && (j & 1) ? d.voff_o : d.voff_e, d.sbase, dbase);
     else
       dma16<kOff, kM0>(NW == 1 && (j & 1) ? d.src_o : d.src_e, dbase);
   }
@@ -691,7 +702,7 @@ struct Attn {
           }
         };
 #pragma unroll
-        for (int t = 0; t < kTilesAhead; ++t)
+        for (int t = 0; t < kAhead; ++t)
           if (t < ntiles) {
             issue_tile(t, kTileInPage ? __builtin_amdgcn_readfirstlane(page_at(cur_pl)) : 0, cur_inp);
             if (kTileInPage) advance();
@@ -716,15 +727,19 @@ struct Attn {
         for (int t = 0; t < ntiles; ++t) {
           // (iteration t-1 staged the ids of tile t-1+kIdAhead, if any; the
           // prologue stages none after its tiles)
-          if (!kFp8) wait_vm(t + 1 < ntiles, !kTileInPage && t > 0 && t + kIdAhead - 1 < ntiles);
+          // (tile t+1's DMAs, and a page-id DMA issued before them, may
+          // still be in flight when two tiles are; with one, nothing newer)
+          if (!kFp8)
+            wait_vm(kAhead > 1 && t + 1 < ntiles,
+                    kAhead > 1 && !kTileInPage && t > 0 && t + kIdAhead - 1 < ntiles);
           lds_barrier();
-          const bool dma = t + kTilesAhead < ntiles;
+          const bool dma = t + kAhead < ntiles;
           const int base = kv_begin + t * kTileKeys;
           float x[16];
           {
             TileDma d{};  // (defined on every path: a phi with undef would put it in VGPRs)
             auto prep = [&] {
-              d = prep_tile(t + kTilesAhead, kTileInPage ? __builtin_amdgcn_readfirstlane(pg_next) : 0,
+              d = prep_tile(t + kAhead, kTileInPage ? __builtin_amdgcn_readfirstlane(pg_next) : 0,
                             cur_inp);
               if (kTileInPage) {
                 advance();
@@ -738,10 +753,14 @@ struct Attn {
             // registers to spare there).  The DMAs go under the other
             // k-steps.
             constexpr bool kPrepUnder = NW > 1;
-            if (!kPrepUnder && dma) prep();
+            // (the DMA test at every k-step is a scalar branch on this
+            // wave-uniform value; as a plain bool it was rebuilt by VALU
+            // instructions on the path of each DMA)
+            const int dma_s = __builtin_amdgcn_readfirstlane(dma ? 1 : 0);
+            if (!kPrepUnder && dma_s) prep();
             scores(stage(t), kpe_slot(t), q, x, [&](auto kc) {
               constexpr int k = decltype(kc)::value;
-              if (!dma) return;
+              if (!dma_s) return;
               if constexpr (k == 0) {
                 if (kPrepUnder) prep();
               } else {
@@ -1042,28 +1061,33 @@ struct Attn {
   }
 };
 
-template <int NW, bool kTileInPage, bool kFp8>
+template <int NW, bool kTileInPage, bool kFp8, bool kCompact>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attention_kernel(AttnArgs args) {
-  __shared__ __attribute__((aligned(1024))) char smem[Attn<NW, kTileInPage, kFp8>::kLdsBytes];
-  Attn<NW, kTileInPage, kFp8> k(args, smem);
+  __shared__ __attribute__((aligned(1024)))
+  char smem[Attn<NW, kTileInPage, kFp8, kCompact>::kLdsBytes];
+  Attn<NW, kTileInPage, kFp8, kCompact> k(args, smem);
   k.run();
 }
 
-template <int NW, bool kFp8>
+template <int NW, bool kFp8, bool kCompact = false>
 hipError_t launch_nw(const AttnArgs& a, int num_workers, hipStream_t stream) {
   if (a.page_size % kTileKeys == 0)
-    hipLaunchKernelGGL((attention_kernel<NW, true, kFp8>), dim3(num_workers), dim3(NW * kWave), 0,
-                       stream, a);
+    hipLaunchKernelGGL((attention_kernel<NW, true, kFp8, kCompact>), dim3(num_workers),
+                       dim3(NW * kWave), 0, stream, a);
   else
-    hipLaunchKernelGGL((attention_kernel<NW, false, kFp8>), dim3(num_workers), dim3(NW * kWave),
-                       0, stream, a);
+    hipLaunchKernelGGL((attention_kernel<NW, false, kFp8, kCompact>), dim3(num_workers),
+                       dim3(NW * kWave), 0, stream, a);
   return hipGetLastError();
 }
 
 template <bool kFp8>
 hipError_t launch_dtype(const AttnArgs& a, int num_workers, hipStream_t stream) {
-  if (a.num_heads <= 32) return launch_nw<1, kFp8>(a, num_workers, stream);
+  if (a.num_heads <= 32) {
+    if constexpr (!kFp8)
+      if (a.compact) return launch_nw<1, false, true>(a, num_workers, stream);
+    return launch_nw<1, kFp8>(a, num_workers, stream);
+  }
   if (a.num_heads <= 64) return launch_nw<2, kFp8>(a, num_workers, stream);
   return launch_nw<4, kFp8>(a, num_workers, stream);
 }

@@ -29,9 +29,12 @@ __device__ __forceinline__ float bf16_hi(unsigned w) {
 // head): lane l owns columns 8l .. 8l+7.  The first batch of partial rows is
 // loaded together with the pieces' LSEs (lane k holds s_k), so a token split
 // in at most kBatch pieces costs one memory round trip; the weights come
-// from the LSE lanes by readlane.
+// from the LSE lanes by readlane.  Batches of 4 rows keep the kernel at 8
+// waves per SIMD, so a decode batch's (token, head) waves (64 x 128) are all
+// resident at once: the latency-bound kernel then costs one round trip of
+// its waves, where batches of 8 needed two.
 __global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeArgs a) {
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 4;
   const int lane = threadIdx.x & 63;
   const int H = a.num_heads;
   const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
