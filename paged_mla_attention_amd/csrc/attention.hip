@@ -160,14 +160,17 @@ __device__ __forceinline__ int opaque(int v) {
 // slot) tile t+1 reuses: no other wave reads those columns in P . V, and
 // the scores of tile t-1 were done before this iteration's barrier.  So two
 // bf16 stages and two raw slots suffice, with the DMAs still two tiles ahead.
-// A compact one-wave variant (kCompact, bf16 cache): two ckv stages and two
-// kpe slots with one tile in flight, 80 KiB of LDS, so that two workgroups
-// share a compute unit (the host plans two workers per compute unit for it).
+// A compact one-wave variant (kCompact) in 80 KiB of LDS, so that two
+// workgroups share a compute unit (the host plans two workers per compute
+// unit for it).  bf16 cache: two ckv stages and two kpe slots with one tile
+// in flight.  fp8 cache: one bf16 stage and kpe slot (a lone wave finishes
+// P . V of tile t before it converts tile t+1 into the same stage) and two
+// raw slots, with two tiles in flight.
 template <int NW, bool kTileInPage, bool kFp8, bool kCompact>
 struct Attn {
-  static_assert(!kCompact || (NW == 1 && !kFp8), "the compact variant is one wave, bf16");
+  static_assert(!kCompact || NW == 1, "the compact variant is one wave");
   // Tiles whose DMAs are in flight beyond the one being computed.
-  static constexpr int kAhead = kCompact ? 1 : kTilesAhead;
+  static constexpr int kAhead = kCompact && !kFp8 ? 1 : kTilesAhead;
   static constexpr int kDimBlocks = (kLoraRank / 32) / NW;  // 32-column blocks of O per wave
   // DMA instructions per tile per wave: bf16 36 / NW; fp8 16 / NW ckv + 4 / NW kpe.
   static constexpr int kCkvLoads = kFp8 ? 16 / NW : 0;
@@ -175,8 +178,8 @@ struct Attn {
   static constexpr int kLoadsPerWave = kFp8 ? kCkvLoads + kKpeLoads : kDmaPerTile / NW;
   static_assert(kDmaPerTile % NW == 0 && (kLoraRank / 32) % NW == 0, "NW must be 1, 2 or 4");
   static_assert(kLoadsPerWave <= 63, "vmcnt holds at most 63");
-  static constexpr int kNStages = kFp8 || kCompact ? 2 : kStages;  // bf16 ckv stages
-  static constexpr int kNKpe = kFp8 || kCompact ? 2 : kKpeSlots;     // bf16 kpe slots
+  static constexpr int kNStages = kFp8 ? (kCompact ? 1 : 2) : (kCompact ? 2 : kStages);  // bf16 ckv stages
+  static constexpr int kNKpe = kFp8 ? (kCompact ? 1 : 2) : (kCompact ? 2 : kKpeSlots);     // bf16 kpe slots
   static constexpr int kStageB = kNStages * kCkvBytes;
   static constexpr int kKpeO = kStageB;
   // fp8 raw ring: two slots of 18 KiB, wave w's slice at w * kRawWaveBytes
@@ -212,7 +215,7 @@ struct Attn {
   static constexpr int kFinWaveBytes = 32 * kFinRow * 4;
   static constexpr int kXchgOff = NW * kFinWaveBytes;  // 1/l of every head slot
   // (a lone wave reads its redo flags before its finish staging covers them)
-  static_assert(kXchgOff + 32 * NW * 4 <= (kFp8 ? kRawOff : (kCompact ? kPOff : kStageB)),
+  static_assert(kXchgOff + 32 * NW * 4 <= (kCompact ? kPOff : (kFp8 ? kRawOff : kStageB)),
                 "finish staging fits the stages (and kpe slots)");
 
   const AttnArgs& a;
@@ -895,9 +898,11 @@ struct Attn {
   // returns the lane's largest scaled score and folds it into m_seen.
   __device__ __forceinline__ float softmax_max(float (&x)[16], int base, float& m_seen) const {
     if (__builtin_expect(base + kTileKeys > kv_end, 0)) {  // the item's last tile only
+      // (made here from the lane id: kept for the kernel, it was spilled)
+      const int h4 = 4 * (opaque(lane) >> 5);
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int key = base + 8 * (j >> 2) + 4 * half + (j & 3);
+        const int key = base + 8 * (j >> 2) + h4 + (j & 3);
         x[j] = key < kv_end ? x[j] : -INFINITY;
       }
     }
@@ -1084,8 +1089,7 @@ hipError_t launch_nw(const AttnArgs& a, int num_workers, hipStream_t stream) {
 template <bool kFp8>
 hipError_t launch_dtype(const AttnArgs& a, int num_workers, hipStream_t stream) {
   if (a.num_heads <= 32) {
-    if constexpr (!kFp8)
-      if (a.compact) return launch_nw<1, false, true>(a, num_workers, stream);
+    if (a.compact) return launch_nw<1, kFp8, true>(a, num_workers, stream);
     return launch_nw<1, kFp8>(a, num_workers, stream);
   }
   if (a.num_heads <= 64) return launch_nw<2, kFp8>(a, num_workers, stream);

@@ -202,7 +202,7 @@ mla_status mla_plan_create(mla_plan_t* out, int32_t device, int32_t num_heads,
   p->page_size = page_size;
   p->cus = cus > 0 ? cus : 1;
   // One-wave kernels (at most 32 heads) run two workgroups per compute
-  // unit on a bf16 cache, so the planner balances over twice the units.
+  // unit, so the planner balances over twice the units.
   p->num_workers = p->cus * (num_heads <= 32 ? 2 : 1);
   for (auto& sl : p->slot) {
     e = hipEventCreateWithFlags(&sl.done, hipEventDisableTiming);
@@ -531,7 +531,7 @@ mla_status run_impl(mla_plan_t p, const void* q_nope, const void* q_pe, const vo
   a.page_size = p->page_size;
   a.scale_log2 = p->scale_log2;
   a.out_scale = kv_cache8 ? kv_scale : 1.f;
-  a.compact = !kv_cache8 && p->num_heads <= 32 && p->num_workers == 2 * p->cus;
+  a.compact = p->num_heads <= 32 && p->num_workers == 2 * p->cus;
   // A schedule read from the host slot: the attention workgroups report when
   // they are done with it (no event between the kernels; runs of one plan
   // are stream-ordered, so a slot's flags only grow), and the merge list
