@@ -352,6 +352,22 @@ struct Attn {
       dma16s<0, 32768 + j * 1024>(voff, qp, dst);
     });
   }
+  // One-wave kernels load the query rows straight into the MFMA operand
+  // registers instead: q[ks] of lane (l32, half) is dims 16 ks + 8 half ..
+  // +8 of head l32 (q_nope for ks < 32, q_pe after), sixteen bytes per load.
+  // (With several waves the scattered loads cost the CU's address path more
+  // than LDS staging does.)
+  __device__ __forceinline__ void load_query(int H, u32x4_t (&q)[kQSteps]) const {
+    const int lane = opaque(this->lane);  // (addresses made per item)
+    const int l32 = lane & 31, half = lane >> 5;
+    const int h0 = wave * 32 + l32;
+    const int64_t h = static_cast<int64_t>(token) * H + (h0 < H ? h0 : 0);
+    const u32x4_t* qn = reinterpret_cast<const u32x4_t*>(a.q_nope + h * kLoraRank) + half;
+    const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(a.q_pe + h * kRopeDim) + half;
+#pragma unroll
+    for (int ks = 0; ks < kQSteps; ++ks)
+      q[ks] = ks < kLoraRank / 16 ? qn[2 * ks] : qp[2 * (ks - kLoraRank / 16)];
+  }
   // LDS offset of this lane's query operand for k-step ks.
   __device__ __forceinline__ int query_lds_off(int ks, int lane) const {
     const int l32 = lane & 31, half = lane >> 5;
@@ -663,12 +679,16 @@ struct Attn {
         // exchange slots the previous item's finish may still be reading.)
         lds_barrier();
         if (ntiles == 0) break;
-        // This wave's query rows go through LDS: whole rows per DMA, where
-        // loading them straight into the MFMA operand layout would touch
-        // 32 rows per load (see stage_query).  The page ids go out in the
-        // same wait, also by DMA: the item's page list (tiles that never
-        // span pages) or the first tiles' per-key ids (tiles that may).
-        stage_query(H);
+        // This wave's query rows go through LDS (several waves): whole rows
+        // per DMA, where loading them straight into the MFMA operand layout
+        // would touch 32 rows per load (see stage_query).  The page ids go
+        // out in the same wait, also by DMA: the item's page list (tiles
+        // that never span pages) or the first tiles' per-key ids (tiles that
+        // may).  A lone wave loads its query after the first tiles' DMAs
+        // instead, so that their latencies overlap (its query staging would
+        // cover the stages).
+        constexpr bool kQueryDirect = NW == 1;
+        if (!kQueryDirect) stage_query(H);
         int n_pages = 1;
         if (kTileInPage) {
           const int P = a.page_size;
@@ -684,16 +704,16 @@ struct Attn {
         // Query as the B operand of the 32x32x16 score MFMAs: lane (l32,
         // half) holds head 32 wave + l32, dims 16 ks + 8 half .. +8.
         u32x4_t q[kQSteps];
-        {
+        if (!kQueryDirect) {
           const int qlane = opaque(lane);
 #pragma unroll
           for (int ks = 0; ks < kQSteps; ++ks)
             q[ks] = *reinterpret_cast<const u32x4_t*>(smem + query_lds_off(ks, qlane));
-        }
 #pragma unroll
-        for (int ks = 0; ks < kQSteps; ++ks) asm volatile("" : : "v"(q[ks]));
-        // Every wave has its query in registers, and the page list is
-        // complete.
+          for (int ks = 0; ks < kQSteps; ++ks) asm volatile("" : : "v"(q[ks]));
+        }
+        // Every wave has its query in registers (several waves), and the
+        // page list is complete.
         lds_barrier();
         // Page-list cursor: entry and first row of the next tile to load.
         int cur_pl = 0, cur_inp = kTileInPage ? kv_begin % a.page_size : 0;
@@ -710,6 +730,14 @@ struct Attn {
             issue_tile(t, kTileInPage ? __builtin_amdgcn_readfirstlane(page_at(cur_pl)) : 0, cur_inp);
             if (kTileInPage) advance();
           }
+        if (kQueryDirect) {
+          // Waited for here, with the first tiles issued before it: a wait
+          // the compiler placed at the first use inside the key loop would
+          // drain the DMAs in flight at every tile.
+          load_query(H, q);
+#pragma unroll
+          for (int ks = 0; ks < kQSteps; ++ks) asm volatile("" : : "v"(q[ks]));
+        }
         // The next tile's page id, read a tile ahead.
         int pg_next = kTileInPage ? page_at(min(cur_pl, n_pages - 1)) : 0;
         if constexpr (kFp8) {
