@@ -299,8 +299,12 @@ const char* mla_last_error(void);
  *   a partial result (normalised output and LSE) into partial slot `slot`.
  * Merge entry (4 int32 each): {token, first_slot, num_slots, 0}: the token's
  *   result is the LSE merge of partial slots [first_slot, first_slot+num_slots).
- * worker_indptr[num_workers+1]: worker w (workgroup w of the attention
- *   launch) runs items [worker_indptr[w], worker_indptr[w+1]) in order.
+ * worker_indptr[num_workers+2]: worker w (workgroup w of the attention
+ *   launch) runs items [worker_indptr[w], worker_indptr[w+1]) in order;
+ *   items [worker_indptr[num_workers], worker_indptr[num_workers+1]) are a
+ *   shared pool of whole-token items (slot -1) that the workgroups take one
+ *   at a time, in order, once their own items are done (empty unless the
+ *   batch has many query tokens).
  * ------------------------------------------------------------------------ */
 typedef struct mla_schedule_s* mla_schedule_t;
 
@@ -314,7 +318,7 @@ mla_status mla_schedule_build(mla_schedule_t* out, const int32_t* qo_indptr,
 void mla_schedule_sizes(mla_schedule_t s, int32_t* num_workers, int64_t* num_items,
                         int64_t* num_merges, int64_t* num_slots);
 
-/* Copy the schedule out: worker_indptr [num_workers+1], items [num_items*8],
+/* Copy the schedule out: worker_indptr [num_workers+2], items [num_items*8],
  * merges [num_merges*4] (host memory, sized from mla_schedule_sizes). */
 void mla_schedule_copy(mla_schedule_t s, int32_t* worker_indptr, int32_t* items,
                        int32_t* merges);

@@ -408,7 +408,9 @@ def run_noalloc(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, q_nope, q_pe
 def schedule(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, page_size: int,
              num_cache_pages: int, num_heads: int, num_workers: int, causal: bool = True,
              lib_path: Optional[str] = None) -> dict:
-    """Run the host planner and return its schedule as numpy arrays."""
+    """Run the host planner and return its schedule as numpy arrays:
+    worker_indptr [num_workers + 2] (the last two entries bound the shared
+    pool), items [num_items, 8], merges [num_merges, 4]."""
     lib = _native.load(lib_path or _native.LIB_PATH, host_only=True)
     qo, kv = _host_i32(qo_indptr), _host_i32(kv_indptr)
     idx, last = _host_i32(kv_indices), _host_i32(kv_last_page_len)
@@ -422,7 +424,7 @@ def schedule(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, page_size: int,
         w, n, m, s = c_int32(), c_int64(), c_int64(), c_int64()
         lib.mla_schedule_sizes(h, ctypes.byref(w), ctypes.byref(n), ctypes.byref(m),
                                ctypes.byref(s))
-        wi = np.zeros(w.value + 1, np.int32)
+        wi = np.zeros(w.value + 2, np.int32)
         items = np.zeros((n.value, 8), np.int32)
         merges = np.zeros((m.value, 4), np.int32)
         lib.mla_schedule_copy(h, _ptr(wi), _ptr(items), _ptr(merges))

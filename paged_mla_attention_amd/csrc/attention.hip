@@ -618,7 +618,7 @@ struct Attn {
     // its page list goes out to LDS now, with that read still in flight.
     // The entry reads (first item, worker_indptr pair) go out together as
     // one lane-parallel load: lanes 0..7 the item's fields, lanes 8 and 9
-    // this worker's item range.
+    // this worker's item range, lanes 10 and 11 the shared pool's.
     const bool fast_first = kTileInPage && a.first_items != nullptr;
     if (fast_first && wave == 0)
       dma4(a.first_pages + blockIdx.x * kFirstPages + lane, lds_base + kPageOff);
@@ -630,6 +630,8 @@ struct Attn {
         src = reinterpret_cast<const int*>(a.first_items) + blockIdx.x * 8 + l;
       else if (l == 8 || l == 9)
         src = a.worker_indptr + blockIdx.x + (l - 8);
+      else if (l == 10 || l == 11)
+        src = a.worker_indptr + gridDim.x + (l - 10);
       if (src) entry = *src;
     }
     const int f_token = __builtin_amdgcn_readlane(entry, 0);
@@ -640,9 +642,39 @@ struct Attn {
     const int f_pages = __builtin_amdgcn_readlane(entry, 7);  // (pad[1]: the page list is staged)
     const int w_begin = __builtin_amdgcn_readlane(entry, 8);
     const int w_end = __builtin_amdgcn_readlane(entry, 9);
+    const int pool_begin = __builtin_amdgcn_readlane(entry, 10);
+    const int pool_n = __builtin_amdgcn_readlane(entry, 11) - pool_begin;
     const int H = a.num_heads;
 
-    for (int it = w_begin; it < w_end; ++it) {
+    // The shared pool (a schedule with many query tokens): once its own
+    // items are done, the workgroup takes pool items one at a time.  Wave 0
+    // asks for the next one (an atomic on a device counter) before the
+    // finish of the item ahead of it, whose output stores cover the atomic's
+    // latency; the index reaches the other waves through LDS.  (The vector
+    // memory counter completes in order, so an atomic issued any earlier
+    // would hold up the key loop's DMA waits.)
+    int popped = 0;  // wave 0, lane 0: the pool index for the next pool item
+    auto pop = [&] {
+      if (wave == 0 && lane == 0)
+        popped = __hip_atomic_fetch_add(a.pool_ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    if (pool_n > 0 && w_begin == w_end) pop();
+
+    for (int next = w_begin;;) {
+      int it;
+      if (next < w_end) {
+        it = next++;
+      } else {
+        if (pool_n <= 0) break;
+        // (the page-list area: no wave reads it until after the item's
+        // first barrier, and its DMA is issued after that barrier)
+        int* xfer = reinterpret_cast<int*>(smem + kPageOff);
+        if (wave == 0 && lane == 0) *xfer = popped;
+        lds_barrier();
+        const int k = __builtin_amdgcn_readfirstlane(*xfer);
+        if (k >= pool_n) break;
+        it = pool_begin + k;
+      }
       // (the first item of a host-slot schedule was read at entry)
       const bool pre = fast_first && it == w_begin;
       if (pre) {
@@ -851,6 +883,7 @@ struct Attn {
         if (!any_redo) break;
         m_ref = fmaxf(m_seen, __shfl_xor(m_seen, 32));  // the head's largest score
       }
+      if (pool_n > 0 && next >= w_end) pop();  // the next item comes from the pool
       finish(o, m_ref, l_run);
     }
     // Every read of the schedule (items, page lists) has been consumed by
@@ -858,6 +891,17 @@ struct Attn {
     // tell the host this workgroup is done with the slot.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
+    if (pool_n > 0 && wave == 0 && lane == 0) {
+      // This workgroup has drawn past the pool's end; the last one to do so
+      // leaves the counters at zero for the next run (every draw of every
+      // workgroup has returned by then).
+      const int d = __hip_atomic_fetch_add(a.pool_ctr + 1, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      if (d == static_cast<int>(gridDim.x) - 1) {
+        __hip_atomic_store(a.pool_ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.pool_ctr + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
     if (a.done_flags && wave == 0 && lane == 0)
       __hip_atomic_store(a.done_flags + blockIdx.x, a.run_seq, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_SYSTEM);

@@ -118,6 +118,9 @@ struct mla_plan_s {
   // denominator), then fp32 lse [slots, H].
   float* d_part = nullptr;
   size_t part_cap = 0;  // 4-byte words
+  // Shared-pool counters (next item, workgroups done): zeroed once here,
+  // left at zero by every run's last workgroup.
+  int32_t* d_pool = nullptr;
 
 };
 
@@ -169,6 +172,7 @@ void release(mla_plan_s* p) {
   }
   if (p->d_stage) (void)hipFree(p->d_stage);
   if (p->d_part) (void)hipFree(p->d_part);
+  if (p->d_pool) (void)hipFree(p->d_pool);
   delete p;
 }
 
@@ -217,6 +221,13 @@ mla_status mla_plan_create(mla_plan_t* out, int32_t device, int32_t num_heads,
       return hip_fail(e, "hipHostMalloc(flags)");
     }
     std::memset(sl.flags, 0, p->num_workers * sizeof(int32_t));
+  }
+  e = hipMalloc(reinterpret_cast<void**>(&p->d_pool), 4 * sizeof(int32_t));
+  if (e == hipSuccess) e = hipMemset(p->d_pool, 0, 4 * sizeof(int32_t));
+  if (e == hipSuccess) e = hipDeviceSynchronize();  // (zero before any stream's first run)
+  if (e != hipSuccess) {
+    release(p);
+    return hip_fail(e, "pool counters");
   }
   *out = p;
   return MLA_OK;
@@ -350,7 +361,8 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
   // list then goes to the merge kernel as kernel arguments.
   const bool direct = !p->reserved &&
                       s.items.size() <= 2 * static_cast<size_t>(p->num_workers) &&
-                      s.merges.size() <= static_cast<size_t>(mla::kInlineMerges);
+                      s.merges.size() <= static_cast<size_t>(mla::kInlineMerges) &&
+                      s.worker_indptr[s.num_workers] == s.worker_indptr[s.num_workers + 1];
   // Each worker's first item, and its page list (up to kFirstPages pages),
   // at fixed places: the kernel reads them without a dependent read.
   const bool first_fast = direct && p->page_size % mla::kTileKeys == 0;
@@ -523,6 +535,7 @@ mla_status run_impl(mla_plan_t p, const void* q_nope, const void* q_pe, const vo
   auto& sl = p->slot[p->cur];
   const char* d = p->direct ? sl.h_stage : p->d_stage;
   a.worker_indptr = reinterpret_cast<const int32_t*>(d + p->off_wi);
+  a.pool_ctr = p->d_pool;
   if (p->reserved) a.scale_log2_ptr = reinterpret_cast<const float*>(d);
   a.items = reinterpret_cast<const mla::WorkItem*>(d + p->off_items);
   a.kv_indptr = reinterpret_cast<const int32_t*>(d + p->off_kv_indptr);

@@ -18,8 +18,14 @@ struct AttnArgs {
   float* lse;                // fp32 [T, H] or nullptr
   uint16_t* part_o;          // bf16 [slots, H, 512], normalised output of each piece
   float* part_lse;           // fp32 [slots, H], natural-log LSE of the piece
+  // [workgroups + 2]: workgroup w's own items, then the shared pool's range
+  // (worker_indptr[workgroups] .. worker_indptr[workgroups + 1]).
   const int32_t* worker_indptr;
   const WorkItem* items;
+  // Device counters of the shared pool, zero between runs: [0] the next pool
+  // item to hand out, [1] workgroups done with the pool (the last one resets
+  // both).  Used only when the pool is not empty.
+  int32_t* pool_ctr;
   const int32_t* kv_indptr;
   const int32_t* kv_indices;
   int32_t num_heads;

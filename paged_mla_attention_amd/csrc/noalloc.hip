@@ -40,8 +40,8 @@ constexpr int kNaMaxDevices = 64;
 constexpr size_t na_align(size_t x) { return (x + 255) / 256 * 256; }
 // Byte offsets of the sections of `scratch`.
 constexpr size_t kOffHdr = 0;  // int32 [0] unused, [1] merge count, [2] status (1: table rejected)
-constexpr size_t kOffWi = 256;                                             // int32 [W + 1]
-constexpr size_t kOffItems = kOffWi + na_align(4 * (kNaMaxWorkers + 1));   // WorkItem [items]
+constexpr size_t kOffWi = 256;                                             // int32 [W + 2]
+constexpr size_t kOffItems = kOffWi + na_align(4 * (kNaMaxWorkers + 2));   // WorkItem [items]
 constexpr size_t kOffMerges = kOffItems + na_align(sizeof(WorkItem) * kNaMaxItems);
 constexpr size_t kOffTokRow = kOffMerges + na_align(sizeof(MergeItem) * kNaMaxTokens);
 constexpr size_t kOffTokTiles = kOffTokRow + na_align(4 * kNaMaxTokens);
@@ -237,6 +237,7 @@ __global__ __launch_bounds__(kPlanThreads) void na_plan_kernel(NaPlanArgs a) {
     // One empty item per token, spread evenly over the workers.
     for (int p = tid; p <= W; p += kPlanThreads)
       wi[p] = static_cast<int32_t>((static_cast<int64_t>(T) * p) / W);
+    if (tid == 0) wi[W + 1] = T;  // (no shared pool)
     for (int t = tid; t < T; t += kPlanThreads)
       items[t] = WorkItem{t, 0, 0, 0, -1, 0, {0, 0}};
     if (tid == 0) {
@@ -282,6 +283,7 @@ __global__ __launch_bounds__(kPlanThreads) void na_plan_kernel(NaPlanArgs a) {
       acc += counts[logical_of(p)];
     }
     wi[W] = acc;
+    wi[W + 1] = acc;  // (no shared pool)
     hdr[1] = static_cast<int32_t>(n_merges);
     hdr[2] = 0;
   }

@@ -30,9 +30,10 @@ struct TokenWork {
 
 // Cost of one work item in units of one key tile (32 latent rows, 36 KiB),
 // fitted to per-workgroup timings on MI355X: at 128 heads a tile costs about
-// 4.5K cycles and an item's fixed part (query load, pipeline fill and drain,
-// output) about 31K, i.e. seven tiles; writing a partial (fp32 output of all
-// heads) adds under one.
+// 3.3-3.8K cycles and an item's fixed part (query load, pipeline fill and
+// drain, output) 24-28K, i.e. seven tiles; a partial output (bf16 rows of all
+// heads) takes the workgroup no longer to write than a final one, and the
+// split's one-tile charge stands for its share of the merge kernel.
 struct CostModel {
   double item;
   double split;
@@ -41,6 +42,17 @@ struct CostModel {
 };
 
 constexpr int kMinPieceTiles = 2;
+
+// The shared pool.  The compute units of one device do not run at one speed:
+// under the sustained MFMA load of a prefill the XCDs' clocks differ by up to
+// 10%, so workgroups with equal static loads end that far apart.  A batch of
+// many query tokens keeps its smallest whole-token items (up to kPoolShare of
+// the work, none larger than 1/kPoolItemDiv of a worker's share) out of the
+// static lists; workgroups take them, largest first, as their own lists run
+// out.  Pool items are never split, so who runs them changes no result.
+constexpr double kPoolShare = 0.10;
+constexpr int kPoolItemDiv = 8;
+constexpr int kPoolMinTokensPerWorker = 4;
 
 // Greedy contiguous fill of `budget` cost per worker; *max_load receives
 // the largest worker cost (above the budget only where the last worker had
@@ -211,6 +223,37 @@ mla_status build_schedule(const PlanArgs& a, Schedule* out) {
   double total = 0.0;
   for (const TokenWork& tw : toks) total += tw.tiles + cm.item;
   const int32_t W = a.num_workers;
+
+  // The pool: smallest whole-token items first, up to kPoolShare of the
+  // work; then ordered largest first.  The static lists take the rest, in
+  // token order.
+  std::vector<TokenWork> pool;
+  if (static_cast<int64_t>(toks.size()) >= int64_t(kPoolMinTokensPerWorker) * W) {
+    const double cap = total / W / kPoolItemDiv;
+    std::vector<int32_t> order;
+    order.reserve(toks.size());
+    for (int32_t i = 0; i < static_cast<int32_t>(toks.size()); ++i)
+      if (toks[i].tiles + cm.item <= cap && toks[i].tiles <= kMaxItemTiles) order.push_back(i);
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int32_t x, int32_t y) { return toks[x].tiles < toks[y].tiles; });
+    std::vector<char> in_pool(toks.size(), 0);
+    double pooled = 0.0;
+    for (const int32_t i : order) {
+      const double c = toks[i].tiles + cm.item;
+      if (pooled + c > kPoolShare * total) break;
+      pooled += c;
+      in_pool[i] = 1;
+    }
+    if (pooled > 0.0) {
+      std::vector<TokenWork> rest;
+      rest.reserve(toks.size());
+      for (size_t i = 0; i < toks.size(); ++i) (in_pool[i] ? pool : rest).push_back(toks[i]);
+      std::stable_sort(pool.begin(), pool.end(),
+                       [](const TokenWork& x, const TokenWork& y) { return x.tiles > y.tiles; });
+      toks.swap(rest);
+      total -= pooled;
+    }
+  }
   // Smallest per-worker budget whose greedy fill fits on W workers (split
   // costs are only known after a fill, so search for it).
   std::vector<WorkItem> items;
@@ -227,8 +270,11 @@ mla_status build_schedule(const PlanArgs& a, Schedule* out) {
     const double mid = 0.5 * (lo + hi);
     if (fits(mid)) hi = mid; else lo = mid;
   }
-  items.reserve(toks.size() + 2 * static_cast<size_t>(W));
+  items.reserve(toks.size() + pool.size() + 2 * static_cast<size_t>(W));
   fill<true>(toks, cm, hi, W, &items, &first, &max_load);
+  const size_t n_static = items.size();
+  for (const TokenWork& tw : pool)
+    items.push_back(WorkItem{tw.token, tw.row, 0, tw.visible, -1, 0, {0, 0}});
 
   // Partial slots: tokens that ended up in more than one item.
   std::vector<int32_t> pieces(static_cast<size_t>(T), 0);
@@ -265,12 +311,14 @@ mla_status build_schedule(const PlanArgs& a, Schedule* out) {
   } else {
     for (int p = 0; p < W; ++p) logical_of[p] = p;
   }
-  s.worker_indptr.assign(W + 1, 0);
+  s.worker_indptr.assign(W + 2, 0);
   for (int p = 0; p < W; ++p) {
     const int l = logical_of[p];
     s.worker_indptr[p + 1] = s.worker_indptr[p] + (first[l + 1] - first[l]);
     s.items.insert(s.items.end(), items.begin() + first[l], items.begin() + first[l + 1]);
   }
+  s.items.insert(s.items.end(), items.begin() + n_static, items.end());
+  s.worker_indptr[W + 1] = static_cast<int32_t>(s.items.size());
   s.append_rows = std::move(append_rows);
   s.append_error = std::move(append_error);
   s.num_workers = W;

@@ -62,7 +62,11 @@ struct Schedule {
   int64_t num_tokens = 0;
   int64_t num_slots = 0;
   int64_t nnz = 0;                     // kv_indptr[batch]
-  std::vector<int32_t> worker_indptr;  // [num_workers + 1], launch order
+  // [num_workers + 2], launch order: worker w's own items are
+  // [worker_indptr[w], worker_indptr[w + 1]); items [worker_indptr[W],
+  // worker_indptr[W + 1]) form the shared pool, taken one at a time by
+  // whichever workgroup runs out of its own items first.
+  std::vector<int32_t> worker_indptr;
   std::vector<WorkItem> items;
   std::vector<MergeItem> merges;
   // KV append: cache row (page * page_size + slot) of each query token's

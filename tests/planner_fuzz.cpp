@@ -51,10 +51,12 @@ int main(int argc, char** argv) {
     int32_t w = 0;
     int64_t n_items = 0, n_merges = 0, n_slots = 0;
     mla_schedule_sizes(s, &w, &n_items, &n_merges, &n_slots);
-    std::vector<int32_t> wi(w + 1), items(n_items * 8 + 8), merges(n_merges * 4 + 4);
+    std::vector<int32_t> wi(w + 2), items(n_items * 8 + 8), merges(n_merges * 4 + 4);
     mla_schedule_copy(s, wi.data(), items.data(), merges.data());
     mla_schedule_destroy(s);
-    CHECK(w == workers && wi[0] == 0 && wi[w] == n_items);
+    CHECK(w == workers && wi[0] == 0 && wi[w] <= wi[w + 1] && wi[w + 1] == n_items);
+    for (int k = 0; k < w; ++k) CHECK(wi[k] <= wi[k + 1]);
+    for (int64_t i = wi[w]; i < n_items; ++i) CHECK(items[i * 8 + 4] == -1 && items[i * 8 + 2] == 0);
     const int T = qo[B];
     std::vector<long long> covered(T, 0);
     std::vector<int> slot_used(n_slots, 0);

@@ -31,8 +31,13 @@ def _sched(w, workers, host_lib, causal=None):
 
 def _check_invariants(w, s, workers):
     items, merges, wi = s["items"], s["merges"], s["worker_indptr"]
-    assert wi.shape == (workers + 1,) and wi[0] == 0 and wi[-1] == items.shape[0]
+    assert wi.shape == (workers + 2,) and wi[0] == 0 and wi[-1] == items.shape[0]
     assert np.all(np.diff(wi) >= 0)
+    # the shared pool: whole tokens (final outputs), largest first
+    pool = items[wi[workers]:wi[workers + 1]]
+    assert np.all(pool[:, 4] == -1) and np.all(pool[:, 2] == 0)
+    ptiles = (pool[:, 3] + TILE - 1) // TILE
+    assert np.all(np.diff(ptiles) <= 0)
     T = w.num_tokens
     lens = w.kv_lens()
     qo = w.qo_indptr
@@ -90,14 +95,36 @@ def test_schedule_invariants(name, workers, host_lib):
 
 def test_schedule_balances_full_workloads(host_lib):
     """At the decode and prefill workloads' page tables (no tensors needed),
-    the most loaded worker carries at most 25% more key tiles than the mean."""
+    the most loaded worker's own list carries at most 25% more key tiles than
+    the mean of the lists."""
     for w in (W.decode_batch(), W.chunked_prefill()):
         s = _sched(w, 256, host_lib)
         _check_invariants(w, s, 256)
         it, wi = s["items"], s["worker_indptr"]
         tiles = (it[:, 3] - it[:, 2] + TILE - 1) // TILE
-        per = np.add.reduceat(np.r_[tiles, 0], wi[:-1])[:256] * (np.diff(wi) > 0)
-        assert per.max() <= 1.25 * tiles.sum() / 256 + 8
+        own = tiles[:wi[256]]
+        per = np.add.reduceat(np.r_[own, 0], wi[:256])[:256] * (np.diff(wi[:257]) > 0)
+        assert per.max() <= 1.25 * own.sum() / 256 + 8
+
+
+def test_shared_pool_sizes(host_lib):
+    """A batch of many query tokens keeps its smallest whole tokens, about a
+    tenth of the work and each small against a worker's share, in the shared
+    pool; a decode batch (fewer tokens than four per worker) has none."""
+    item_cost = 7.0  # the cost model's fixed part of an item at 128 heads, in tiles
+    s = _sched(W.decode_batch(), 256, host_lib)
+    assert s["worker_indptr"][256] == s["worker_indptr"][257]
+    w = W.chunked_prefill()
+    s = _sched(w, 256, host_lib)
+    it, wi = s["items"], s["worker_indptr"]
+    cost = (it[:, 3] - it[:, 2] + TILE - 1) // TILE + item_cost
+    pool = cost[wi[256]:wi[257]]
+    assert 0.08 * cost.sum() <= pool.sum() <= 0.10 * cost.sum()
+    assert pool.max() <= cost.sum() / 256 / 8
+    # every pooled token is no longer than any whole token left in the lists
+    own = it[:wi[256]]
+    whole = own[own[:, 4] == -1]
+    assert pool.max() - item_cost <= ((whole[:, 3] + TILE - 1) // TILE).min() or len(whole) == 0
 
 
 @pytest.mark.parametrize("workers", [3, 64])
