@@ -1,7 +1,8 @@
 """Edge cases through the C ABI against the fp64 oracle: rows longer than the
 longest work item (split at the item cap as well as for balance), with tiles
 inside pages and with per-key page ids, batches whose queries see no keys,
-an empty batch, a single head, and many short prefill items per worker."""
+an empty batch, a single head, many short prefill items per worker, and
+the shared pool of whole-token items."""
 
 import numpy as np
 import pytest
@@ -118,3 +119,37 @@ def test_reserved_plan_takes_a_long_causal_prefix():
     toks = np.union1d(sample_tokens(w, per_row=4), split_tokens(w)[:16])
     o_ref, l_ref = oracle_of(w, tokens=toks)
     assert_close(o[toks], lse[toks], o_ref, l_ref, "reserved long causal prefix")
+
+
+@pytest.mark.parametrize("heads,page_size", [(64, 64), (128, 16), (32, 64)])
+def test_shared_pool_every_token_and_counter_reset(heads, page_size):
+    """A batch with enough query tokens for the shared pool (whole-token items
+    that workgroups draw from a device counter once their own lists are done):
+    every token checked against the oracle, over two runs of one plan with
+    other queries, so a counter not left at zero by the first run would skip
+    pool items in the second."""
+    import paged_mla_attention_amd as pm
+    from gpu_util import to_dev_bf16
+    rng = np.random.default_rng(97 + heads)
+    workers = torch.cuda.get_device_properties(0).multi_processor_count * (2 if heads <= 32 else 1)
+    n_rows = 8
+    q_len = (4 * workers + n_rows - 1) // n_rows + 3
+    # rows whose first queries see few keys (small items), next to long ones
+    kv = q_len + np.array([0, 1200, 40, 1500, 10, 900, 0, 1300])
+    w = W.make_workload("pool", 0, kv, [q_len] * n_rows, heads, page_size, rng=rng)
+    s = pm.schedule(w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_len, page_size,
+                    w.num_pages, heads, workers)
+    wi = s["worker_indptr"]
+    assert wi[workers + 1] - wi[workers] > workers, "no shared pool for this batch"
+    plan = pm.MLAPlan(heads, page_size)
+    kv_dev = to_dev_bf16(w.kv_cache)
+    try:
+        for rep in range(2):
+            if rep:
+                w.q_nope = W.bf16_normals(rng, w.q_nope.shape)
+                w.q_pe = W.bf16_normals(rng, w.q_pe.shape)
+            o, lse = run_library(w, plan=plan, kv_cache=kv_dev)
+            o_ref, l_ref = oracle_of(w)
+            assert_close(o, lse, o_ref, l_ref, f"shared pool H={heads} P={page_size} run {rep}")
+    finally:
+        plan.close()

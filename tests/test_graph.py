@@ -1,8 +1,8 @@
 """mla_run captured in a HIP graph and replayed: every replay, with eager
 work and synchronisations between the replays, matches the eager result bit
 for bit.  Covers a schedule the kernels read from the pinned host slot
-(decode-sized, released by the kernels' flags) and one read from the
-device copy (prefill-sized)."""
+(decode-sized, released by the kernels' flags), one read from the device
+copy (prefill-sized) and one with a shared pool of whole-token items."""
 
 import numpy as np
 import pytest
@@ -18,7 +18,7 @@ def _dev(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-@pytest.mark.parametrize("shape", ["decode", "prefill"])
+@pytest.mark.parametrize("shape", ["decode", "prefill", "pool"])
 def test_graph_replays_match_eager(shape):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
@@ -26,6 +26,12 @@ def test_graph_replays_match_eager(shape):
     if shape == "decode":
         w = W.make_workload("g_decode", 0, [700, 33, 1500, 64], [1, 1, 1, 1], 128, 64,
                             rng=np.random.default_rng(41))
+    elif shape == "pool":
+        # enough query tokens (and small whole-token items) for the shared
+        # pool, whose device counter every run must leave at zero
+        q_len = (4 * torch.cuda.get_device_properties(0).multi_processor_count + 7) // 8 + 3
+        kv = q_len + np.array([0, 1200, 40, 1500, 10, 900, 0, 1300])
+        w = W.make_workload("g_pool", 0, kv, [q_len] * 8, 128, 64, rng=np.random.default_rng(43))
     else:
         w = W.make_workload("g_prefill", 0, [1200, 300, 2100], [256, 300, 128], 128, 64,
                             rng=np.random.default_rng(42))
