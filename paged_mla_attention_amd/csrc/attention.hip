@@ -162,21 +162,15 @@ __device__ __forceinline__ int opaque(int v) {
 // bf16 stages and two raw slots suffice, with the DMAs still two tiles ahead.
 // A compact one-wave variant (kCompact) in 80 KiB of LDS, so that two
 // workgroups share a compute unit (the host plans two workers per compute
-// unit for it).  bf16 cache: two ckv stages and two kpe slots, still with
-// two tiles in flight: tile t+2 goes into tile t's stage while P . V of
-// tile t reads it, each DMA issued right after the last read of the columns
-// it overwrites (kDmaInPv), and into tile t's kpe slot, which only the
-// scores read.  fp8 cache: one bf16 stage and kpe slot (a lone wave
-// finishes P . V of tile t before it converts tile t+1 into the same stage)
-// and two raw slots, with two tiles in flight.
+// unit for it).  bf16 cache: two ckv stages and two kpe slots with one tile
+// in flight.  fp8 cache: one bf16 stage and kpe slot (a lone wave finishes
+// P . V of tile t before it converts tile t+1 into the same stage) and two
+// raw slots, with two tiles in flight.
 template <int NW, bool kTileInPage, bool kFp8, bool kCompact>
 struct Attn {
   static_assert(!kCompact || NW == 1, "the compact variant is one wave");
   // Tiles whose DMAs are in flight beyond the one being computed.
-  static constexpr int kAhead = kTilesAhead;
-  // The DMAs of tile t+2 go out under P . V of tile t (compact bf16 kernel,
-  // whose two stages hold tiles t and t+1), not under the scores.
-  static constexpr bool kDmaInPv = kCompact && !kFp8;
+  static constexpr int kAhead = kCompact && !kFp8 ? 1 : kTilesAhead;
   static constexpr int kDimBlocks = (kLoraRank / 32) / NW;  // 32-column blocks of O per wave
   // DMA instructions per tile per wave: bf16 36 / NW; fp8 16 / NW ckv + 4 / NW kpe.
   static constexpr int kCkvLoads = kFp8 ? 16 / NW : 0;
@@ -762,16 +756,12 @@ struct Attn {
             ++cur_pl;
           }
         };
-        auto issue_next = [&](int t) {
-          issue_tile(t, kTileInPage ? __builtin_amdgcn_readfirstlane(page_at(cur_pl)) : 0, cur_inp);
-          if (kTileInPage) advance();
-        };
-        // (kDmaInPv: tile 1 after the query's wait, which waits for every
-        // load issued before it, so that tile 1 stays in flight)
-        constexpr int kFirstIssue = kDmaInPv ? 1 : kAhead;
 #pragma unroll
-        for (int t = 0; t < kFirstIssue; ++t)
-          if (t < ntiles) issue_next(t);
+        for (int t = 0; t < kAhead; ++t)
+          if (t < ntiles) {
+            issue_tile(t, kTileInPage ? __builtin_amdgcn_readfirstlane(page_at(cur_pl)) : 0, cur_inp);
+            if (kTileInPage) advance();
+          }
         if (kQueryDirect) {
           // Waited for here, with the first tiles issued before it: a wait
           // the compiler placed at the first use inside the key loop would
@@ -780,9 +770,6 @@ struct Attn {
 #pragma unroll
           for (int ks = 0; ks < kQSteps; ++ks) asm volatile("" : : "v"(q[ks]));
         }
-#pragma unroll
-        for (int t = kFirstIssue; t < kAhead; ++t)
-          if (t < ntiles) issue_next(t);
         // The next tile's page id, read a tile ahead.
         int pg_next = kTileInPage ? page_at(min(cur_pl, n_pages - 1)) : 0;
         if constexpr (kFp8) {
@@ -812,31 +799,31 @@ struct Attn {
           const bool dma = t + kAhead < ntiles;
           const int base = kv_begin + t * kTileKeys;
           float x[16];
-          TileDma d{};  // (defined on every path: a phi with undef would put it in VGPRs)
-          auto prep = [&] {
-            d = prep_tile(t + kAhead, kTileInPage ? __builtin_amdgcn_readfirstlane(pg_next) : 0,
-                          cur_inp);
-            if (kTileInPage) {
-              advance();
-              pg_next = page_at(min(cur_pl, n_pages - 1));
-            } else if (t + kIdAhead < ntiles) {
-              stage_ids(t + kIdAhead);
-            }
-          };
-          // (the DMA test at every k-step is a scalar branch on this
-          // wave-uniform value; as a plain bool it was rebuilt by VALU
-          // instructions on the path of each DMA)
-          const int dma_s = __builtin_amdgcn_readfirstlane(dma ? 1 : 0);
           {
+            TileDma d{};  // (defined on every path: a phi with undef would put it in VGPRs)
+            auto prep = [&] {
+              d = prep_tile(t + kAhead, kTileInPage ? __builtin_amdgcn_readfirstlane(pg_next) : 0,
+                            cur_inp);
+              if (kTileInPage) {
+                advance();
+                pg_next = page_at(min(cur_pl, n_pages - 1));
+              } else if (t + kIdAhead < ntiles) {
+                stage_ids(t + kIdAhead);
+              }
+            };
             // With several waves, the DMA set-up goes under the first
             // k-step's MFMA (a lone wave, with four times the DMAs, has no
             // registers to spare there).  The DMAs go under the other
-            // k-steps (kDmaInPv: under P . V instead).
+            // k-steps.
             constexpr bool kPrepUnder = NW > 1;
-            if (!kDmaInPv && !kPrepUnder && dma_s) prep();
+            // (the DMA test at every k-step is a scalar branch on this
+            // wave-uniform value; as a plain bool it was rebuilt by VALU
+            // instructions on the path of each DMA)
+            const int dma_s = __builtin_amdgcn_readfirstlane(dma ? 1 : 0);
+            if (!kPrepUnder && dma_s) prep();
             scores(stage(t), kpe_slot(t), q, x, [&](auto kc) {
               constexpr int k = decltype(kc)::value;
-              if (kDmaInPv || !dma_s) return;
+              if (!dma_s) return;
               if constexpr (k == 0) {
                 if (kPrepUnder) prep();
               } else {
@@ -865,23 +852,7 @@ struct Attn {
             });
           }
           store_p(p, pbuf(t));
-          if constexpr (kDmaInPv) {
-            // Tile t+2 into tile t's kpe slot (the scores are done with it)
-            // under the first steps, and into tile t's stage under the second
-            // key half: a 32-column block's last read is its step there, and
-            // its two DMAs follow that step.
-            lds_barrier();
-            if (dma_s) prep();
-            pv(stage(t), pbuf(t), o, [&](auto sc) {
-              constexpr int st = decltype(sc)::value;
-              if (!dma_s) return;
-              if constexpr (st < kDmaPerTile - kCkvDmas) issue_one<kCkvDmas + st>(d);
-              if constexpr (st >= kDimBlocks) {
-                issue_one<2 * (st - kDimBlocks)>(d);
-                issue_one<2 * (st - kDimBlocks) + 1>(d);
-              }
-            });
-          } else if (!kPipe) {
+          if (!kPipe) {
             lds_barrier();
             pv(stage(t), pbuf(t), o, [&](auto) {});
           }

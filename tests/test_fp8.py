@@ -2,7 +2,8 @@
 mla_append_kv_fp8), against the fp64 oracle: ragged batches over every
 kernel variant (one, two and four waves; tiles inside pages and per-key
 pages), the full decode and long-decode batches, the overflow-redo path,
-and the quantising append bit for bit."""
+a batch with a shared pool of whole-token items, and the quantising append
+bit for bit."""
 
 import numpy as np
 import pytest
@@ -164,3 +165,30 @@ def test_fp8_rejects_bad_scale():
     for bad in (0.0, -1.0, float("inf"), float("nan")):
         with pytest.raises(_native.MLAError, match="kv_scale"):
             _run_fp8(w, codes, bad)
+
+
+@pytest.mark.parametrize("heads,page_size", [(128, 64), (32, 16)])
+def test_fp8_shared_pool_every_token(heads, page_size):
+    """A batch with a shared pool of whole-token items over an fp8 cache:
+    every token against the fp8 oracle, over two runs of one plan."""
+    import paged_mla_attention_amd as pm
+    rng = np.random.default_rng(410 + heads)
+    workers = torch.cuda.get_device_properties(0).multi_processor_count * (2 if heads <= 32 else 1)
+    q_len = (4 * workers + 7) // 8 + 3
+    kv = q_len + np.array([0, 1200, 40, 1500, 10, 900, 0, 1300])
+    w = W.make_workload("fp8_pool", 0, kv, [q_len] * 8, heads, page_size, rng=rng)
+    s = pm.schedule(w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_len, page_size,
+                    w.num_pages, heads, workers)
+    assert s["worker_indptr"][workers + 1] - s["worker_indptr"][workers] > workers
+    scale = 0.21
+    codes = W.fp8_cache_codes(w.kv_cache, scale)
+    plan = pm.MLAPlan(heads, page_size)
+    try:
+        for rep in range(2):
+            if rep:
+                w.q_nope = W.bf16_normals(rng, w.q_nope.shape)
+            o, lse = _run_fp8(w, codes, scale, plan=plan)
+            o_ref, l_ref = _oracle_fp8(w, codes, scale)
+            assert_close(o, lse, o_ref, l_ref, f"fp8 shared pool H={heads} P={page_size} run {rep}")
+    finally:
+        plan.close()
