@@ -584,6 +584,7 @@ mla_status run_impl(mla_plan_t p, const void* q_nope, const void* q_pe, const vo
     m.lse = lse;
     m.num_heads = p->num_heads;
     m.num_merges = static_cast<int32_t>(s.merges.size());
+    for (const mla::MergeItem& mi : s.merges) m.max_pieces = std::max(m.max_pieces, mi.num_slots);
     if (p->reserved) {  // (captured kernels cover the reserved count)
       m.num_merges = static_cast<int32_t>(p->cap_merges);
       m.num_merges_ptr = reinterpret_cast<const int32_t*>(d + sizeof(float));

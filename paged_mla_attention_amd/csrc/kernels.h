@@ -78,6 +78,7 @@ struct SplitMergeArgs {
   int32_t num_heads;
   int32_t num_merges;             // entries (the grid covers this many)
   const int32_t* num_merges_ptr;  // non-null: the live count, <= num_merges (reserved plans)
+  int32_t max_pieces;             // most pieces of one token, 0 if not known on the host
 };
 
 // Attention over every planned work item: one workgroup per worker.  An

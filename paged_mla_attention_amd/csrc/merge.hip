@@ -32,9 +32,11 @@ __device__ __forceinline__ float bf16_hi(unsigned w) {
 // from the LSE lanes by readlane.  Batches of 4 rows keep the kernel at 8
 // waves per SIMD, so a decode batch's (token, head) waves (64 x 128) are all
 // resident at once: the latency-bound kernel then costs one round trip of
-// its waves, where batches of 8 needed two.
+// its waves, where batches of 8 needed two.  A merge of few (token, head)
+// pairs with many pieces each (a long-context decode: 16 x 16 pairs of 32
+// pieces) has registers to spare and takes them in larger batches.
+template <int kBatch>
 __global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeArgs a) {
-  constexpr int kBatch = 4;
   const int lane = threadIdx.x & 63;
   const int H = a.num_heads;
   const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -137,8 +139,16 @@ __global__ __launch_bounds__(256) void merge_state_kernel(const uint16_t* v_a,
 hipError_t launch_split_merge(const SplitMergeArgs& a, hipStream_t stream) {
   if (a.num_merges <= 0) return hipSuccess;
   const int64_t pairs = static_cast<int64_t>(a.num_merges) * a.num_heads;
-  hipLaunchKernelGGL(split_merge_kernel, dim3(static_cast<unsigned>((pairs + 3) / 4)), dim3(256), 0,
-                     stream, a);
+  const dim3 grid(static_cast<unsigned>((pairs + 3) / 4));
+  // (up to 4096 pairs, 16 waves per compute unit: residency does not limit
+  // the round trips there)
+  const bool few = pairs <= 4096;
+  if (few && a.max_pieces > 16)
+    hipLaunchKernelGGL(split_merge_kernel<32>, grid, dim3(256), 0, stream, a);
+  else if (few && a.max_pieces > 4)
+    hipLaunchKernelGGL(split_merge_kernel<16>, grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(split_merge_kernel<4>, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
