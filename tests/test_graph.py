@@ -144,3 +144,70 @@ def test_reserved_plan_graph_survives_replans():
         plan.plan(big.qo_indptr, big.kv_indptr, big.kv_indices, big.kv_last_page_len,
                   num_cache_pages=big.num_pages)
     plan.close()
+
+
+def test_reserved_plan_graph_with_shared_pool():
+    """A captured run of a plan with reserved capacity, replayed after plans
+    that alternate between a batch with a shared pool of whole-token items
+    and one without: the pool's range comes from the device copy of the
+    schedule and its counters are left at zero by every replay."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_mla_attention_amd as pm
+    import oracle
+    from gpu_util import assert_close
+    H, P = 64, 16
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    q_len = (4 * cus + 7) // 8 + 3
+    kv = q_len + np.array([0, 1200, 40, 1500, 10, 900, 0, 1300])
+    pooled = W.make_workload("rp1", 0, kv, [q_len] * 8, H, P, rng=np.random.default_rng(11))
+    plain = W.make_workload("rp2", 0, [700, 90, 1500], [1, 30, 2], H, P,
+                            rng=np.random.default_rng(12))
+    s = pm.schedule(pooled.qo_indptr, pooled.kv_indptr, pooled.kv_indices,
+                    pooled.kv_last_page_len, P, pooled.num_pages, H, cus)
+    assert s["worker_indptr"][cus + 1] > s["worker_indptr"][cus], "no shared pool"
+    batches = [pooled, plain, pooled]
+    max_t = max(w.num_tokens for w in batches)
+    max_pages = max(w.num_pages for w in batches)
+    max_nnz = max(int(w.kv_indptr[-1]) for w in batches)
+    q_buf = torch.zeros((max_t, H, 512), dtype=torch.bfloat16, device="cuda")
+    qp_buf = torch.zeros((max_t, H, 64), dtype=torch.bfloat16, device="cuda")
+    kv_buf = torch.zeros((max_pages, P, 576), dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros((max_t, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros((max_t, H), dtype=torch.float32, device="cuda")
+    plan = pm.MLAPlan(H, P)
+    plan.reserve(8, max_t, max_nnz)
+
+    def load(w):
+        T = w.num_tokens
+        q_buf[:T].copy_(_dev(w.q_nope))
+        qp_buf[:T].copy_(_dev(w.q_pe))
+        kv_buf[:w.num_pages].copy_(_dev(w.kv_cache))
+        plan.plan(w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_len, causal=True,
+                  sm_scale=w.sm_scale, num_cache_pages=max_pages)
+
+    load(plain)
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        plan.run(q_buf, qp_buf, kv_buf, out=out, lse=lse, stream=st)
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        plan.run(q_buf, qp_buf, kv_buf, out=out, lse=lse)
+    torch.cuda.synchronize()
+    try:
+        for w in batches:
+            load(w)
+            out.fill_(0)
+            g.replay()
+            torch.cuda.synchronize()
+            T = w.num_tokens
+            o = out[:T].view(torch.int16).cpu().numpy().view(np.uint16)
+            o_ref, l_ref = oracle.attention(w.q_nope, w.q_pe, w.kv_cache, w.qo_indptr,
+                                            w.kv_indptr, w.kv_indices, w.kv_last_page_len, P,
+                                            True, w.sm_scale)
+            assert_close(o, lse[:T].cpu().numpy(), o_ref, l_ref, f"replay after planning {w.name}")
+    finally:
+        plan.close()
