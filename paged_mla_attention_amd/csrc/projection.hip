@@ -65,13 +65,24 @@ __device__ __forceinline__ void wave_lds_sync() {
   asm volatile("" ::: "memory");
 }
 
+// The grid is one-dimensional: workgroups go round-robin over the 8 XCDs of
+// the device, each with its own L2, and the kNSplit workgroups that read the
+// same input rows (one (token-block, head) pair, different output columns)
+// are numbered 8 apart, so they run on one XCD at about the same time and
+// all but the first find the rows in its L2.
 template <int K, int N>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void head_matmul_kernel(
-    const uint16_t* x, const uint16_t* w, uint16_t* out, int64_t T, int H) {
+    const uint16_t* x, const uint16_t* w, uint16_t* out, int64_t T, int H, int n_bx) {
   using S = ProjShape<K, N>;
   __shared__ __attribute__((aligned(16))) uint32_t lds[S::kLdsBytes / 4];
-  const int h = blockIdx.y;
-  const int n_base = blockIdx.z * S::kCols;
+  constexpr int kXcds = 8;
+  const int id = blockIdx.x;
+  const int r = id % (kXcds * S::kNSplit);
+  const int pair = (id / (kXcds * S::kNSplit)) * kXcds + r % kXcds;
+  if (pair >= n_bx * H) return;  // (the grid is rounded up to whole groups)
+  const int bx = pair % n_bx;
+  const int h = pair / n_bx;
+  const int n_base = (r / kXcds) * S::kCols;
   // Stage w[h][:, n_base .. n_base + kCols) transposed: task (k pair kp,
   // 8-column group g) reads rows 2 kp and 2 kp + 1 (16 bytes each) and writes
   // eight dwords {w[2kp][n], w[2kp+1][n]} to LDS row n at column 2 kp.
@@ -95,15 +106,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void h
   }
   __syncthreads();
   // The staged weights serve every token block this workgroup takes:
-  // blocks blockIdx.x, blockIdx.x + gridDim.x, ...
+  // blocks bx, bx + n_bx, ...
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, half = lane >> 5;
   const char* lrow = reinterpret_cast<const char*>(lds) + (l32 * S::kRow + 8 * half) * 2;
   char* piece = reinterpret_cast<char*>(lds) + S::kWBytes + wave * S::kPieceBytes;
   // Row-piece task of a lane: token 4 j + lane / 16 of the wave's 32 (j = 0..7),
   // columns 8 (lane % 16) .. + 7 of the piece.
   const int pr = lane >> 4, pc = 8 * (lane & 15);
-  for (int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTok; t0 < T;
-       t0 += static_cast<int64_t>(gridDim.x) * kTok) {
+  for (int64_t t0 = static_cast<int64_t>(bx) * kTok; t0 < T; t0 += static_cast<int64_t>(n_bx) * kTok) {
     const int64_t tw = t0 + 32 * wave;
     if (tw >= T) break;
     f32x16_t acc[S::kNBlocks];
@@ -210,8 +220,11 @@ hipError_t launch(const uint16_t* x, const uint16_t* w, uint16_t* out, int64_t T
   constexpr int kNSplit = ProjShape<K, N>::kNSplit;
   const int64_t per_head = std::max<int64_t>(1, 1024 / (static_cast<int64_t>(H) * kNSplit));
   const int64_t blocks = std::min(need, per_head);
-  hipLaunchKernelGGL((head_matmul_kernel<K, N>), dim3(static_cast<unsigned>(blocks), H, kNSplit),
-                     dim3(256), 0, stream, x, w, out, T, H);
+  const int64_t groups = (blocks * H + 7) / 8;  // of 8 (token-block, head) pairs
+  const int64_t grid = groups * 8 * kNSplit;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((head_matmul_kernel<K, N>), dim3(static_cast<unsigned>(grid)), dim3(256), 0,
+                     stream, x, w, out, T, H, static_cast<int>(blocks));
   return hipGetLastError();
 }
 
