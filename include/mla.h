@@ -141,8 +141,10 @@ mla_status mla_plan_reserve(mla_plan_t plan, int32_t max_batch, int64_t max_toke
  * slot is released by the kernels themselves (each workgroup stores the
  * run's sequence number to pinned memory when it is done with the slot; a
  * later mla_plan waits on those); all runs of one plan must therefore be
- * ordered on one stream.  The plan must not be re-planned while a captured
- * graph that reads it may still replay.
+ * ordered on one stream (they also share the plan's split-KV workspace and
+ * the device counters from which the workgroups draw a batch's shared pool
+ * of whole-token items, which each run leaves at zero).  The plan must not
+ * be re-planned while a captured graph that reads it may still replay.
  *
  * Errors: MLA_E_STATE without a successful mla_plan; MLA_E_INVALID for a NULL
  * required pointer; MLA_E_HIP if a launch fails. */
