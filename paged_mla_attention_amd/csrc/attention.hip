@@ -140,6 +140,17 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// Eight E4M3 codes (two dwords) as eight bf16 values, exactly (every E4M3
+// value is a bf16 value).
+__device__ __forceinline__ u32x4_t cvt_fp8x8(uint32_t w0, uint32_t w1) {
+  u32x4_t o;
+  o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+  o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+  o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+  o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+  return o;
+}
+
 // A per-call copy of a lane value the compiler cannot see through: address
 // arithmetic derived from it stays where it is used instead of being hoisted
 // out of the item loop, where it would occupy (and spill) registers for the
@@ -160,17 +171,17 @@ __device__ __forceinline__ int opaque(int v) {
 // slot) tile t+1 reuses: no other wave reads those columns in P . V, and
 // the scores of tile t-1 were done before this iteration's barrier.  So two
 // bf16 stages and two raw slots suffice, with the DMAs still two tiles ahead.
-// A compact one-wave variant (kCompact) in 80 KiB of LDS, so that two
-// workgroups share a compute unit (the host plans two workers per compute
-// unit for it).  bf16 cache: two ckv stages and two kpe slots with one tile
-// in flight.  fp8 cache: one bf16 stage and kpe slot (a lone wave finishes
-// P . V of tile t before it converts tile t+1 into the same stage) and two
-// raw slots, with two tiles in flight.
+// A compact one-wave variant (kCompact, bf16 stages only) in 80 KiB of LDS,
+// so that two workgroups share a compute unit (the host plans two workers
+// per compute unit for it): two ckv stages and two kpe slots with one tile
+// in flight.  With an fp8 cache the same layout serves the two-wave split
+// kernel (run_split), whose second wave fills the stages from the codes.
 template <int NW, bool kTileInPage, bool kFp8, bool kCompact>
 struct Attn {
   static_assert(!kCompact || NW == 1, "the compact variant is one wave");
+  static_assert(!(kCompact && kFp8), "an fp8 cache with the compact layout runs run_split");
   // Tiles whose DMAs are in flight beyond the one being computed.
-  static constexpr int kAhead = kCompact && !kFp8 ? 1 : kTilesAhead;
+  static constexpr int kAhead = kCompact ? 1 : kTilesAhead;
   static constexpr int kDimBlocks = (kLoraRank / 32) / NW;  // 32-column blocks of O per wave
   // DMA instructions per tile per wave: bf16 36 / NW; fp8 16 / NW ckv + 4 / NW kpe.
   static constexpr int kCkvLoads = kFp8 ? 16 / NW : 0;
@@ -178,8 +189,8 @@ struct Attn {
   static constexpr int kLoadsPerWave = kFp8 ? kCkvLoads + kKpeLoads : kDmaPerTile / NW;
   static_assert(kDmaPerTile % NW == 0 && (kLoraRank / 32) % NW == 0, "NW must be 1, 2 or 4");
   static_assert(kLoadsPerWave <= 63, "vmcnt holds at most 63");
-  static constexpr int kNStages = kFp8 ? (kCompact ? 1 : 2) : (kCompact ? 2 : kStages);  // bf16 ckv stages
-  static constexpr int kNKpe = kFp8 ? (kCompact ? 1 : 2) : (kCompact ? 2 : kKpeSlots);     // bf16 kpe slots
+  static constexpr int kNStages = kFp8 || kCompact ? 2 : kStages;  // bf16 ckv stages
+  static constexpr int kNKpe = kFp8 || kCompact ? 2 : kKpeSlots;     // bf16 kpe slots
   static constexpr int kStageB = kNStages * kCkvBytes;
   static constexpr int kKpeO = kStageB;
   // fp8 raw ring: two slots of 18 KiB, wave w's slice at w * kRawWaveBytes
@@ -907,6 +918,230 @@ struct Attn {
                          __HIP_MEMORY_SCOPE_SYSTEM);
   }
 
+  // fp8 cache, at most 32 heads: two waves per workgroup.  Wave 0 computes
+  // (scores, softmax, P . V and the finish of the compact one-wave kernel
+  // over its two bf16 stages); wave 1, on a SIMD the compact kernel leaves
+  // idle, produces: it loads each tile's E4M3 codes into its registers two
+  // tiles ahead and converts them, exactly, into the bf16 stage and kpe slot
+  // layout the computing wave reads.  One barrier per tile: behind it the
+  // producer has converted tile t+1 into the stage the computing wave
+  // finished with in tile t-1.  Used with the compact bf16 kernel's LDS
+  // layout and launched with 128 threads.
+  __device__ void run_split() {
+    static_assert(NW == 1 && kCompact && !kFp8, "the split kernel uses the compact bf16 layout");
+    // (one loop per role, so that neither carries the other's registers)
+    if (wave == 1)
+      split_loop<true>();
+    else
+      split_loop<false>();
+  }
+  template <bool producer>
+  __device__ __forceinline__ void split_loop() {
+    const bool fast_first = kTileInPage && a.first_items != nullptr;
+    if (fast_first && producer)
+      dma4(a.first_pages + blockIdx.x * kFirstPages + lane, lds_base + kPageOff);
+    int entry = 0;
+    {
+      const int l = opaque(lane);
+      const int* src = nullptr;
+      if (l < 8 && fast_first)
+        src = reinterpret_cast<const int*>(a.first_items) + blockIdx.x * 8 + l;
+      else if (l == 8 || l == 9)
+        src = a.worker_indptr + blockIdx.x + (l - 8);
+      else if (l == 10 || l == 11)
+        src = a.worker_indptr + gridDim.x + (l - 10);
+      if (src) entry = *src;
+    }
+    const int f_token = __builtin_amdgcn_readlane(entry, 0);
+    const int f_begin = __builtin_amdgcn_readlane(entry, 2);
+    const int f_end = __builtin_amdgcn_readlane(entry, 3);
+    const int f_slot = __builtin_amdgcn_readlane(entry, 4);
+    const int f_base = __builtin_amdgcn_readlane(entry, 5);
+    const int f_pages = __builtin_amdgcn_readlane(entry, 7);
+    const int w_begin = __builtin_amdgcn_readlane(entry, 8);
+    const int w_end = __builtin_amdgcn_readlane(entry, 9);
+    const int pool_begin = __builtin_amdgcn_readlane(entry, 10);
+    const int pool_n = __builtin_amdgcn_readlane(entry, 11) - pool_begin;
+    const int H = a.num_heads;
+
+    // (the shared pool as in run(): the computing wave draws, through LDS)
+    int popped = 0;
+    auto pop = [&] {
+      if (wave == 0 && lane == 0)
+        popped = __hip_atomic_fetch_add(a.pool_ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    if (pool_n > 0 && w_begin == w_end) pop();
+
+    // Producer: this lane's key of a tile and which 16-column chunks of it
+    // (c = 2 j + half, j = 0 .. 17) it converts.
+    constexpr int kRawLoads = kLatentDim / 32;  // 18 x 16 bytes per lane
+    typedef u32x4_t RawTile[kRawLoads];
+    auto raw_load = [&](int t, int pg, RawTile& r) {
+      const int key = min(kv_begin + t * kTileKeys + opaque(l32), kv_end - 1);
+      const int P = a.page_size;
+      int64_t row;
+      if (kTileInPage) {
+        row = static_cast<int64_t>(pg) * P + key % P;
+      } else {
+        const int p = a.kv_indices[page_base + (P == 1 ? key : key / P)];
+        row = P == 1 ? p : static_cast<int64_t>(p) * P + key % P;
+      }
+      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.kv_cache8 + row * kLatentDim) + half;
+#pragma unroll
+      for (int j = 0; j < kRawLoads; ++j) r[j] = src[2 * j];
+    };
+    auto raw_store = [&](int t, const RawTile& r) {
+      char* stg = smem + (t % kNStages) * kCkvBytes;
+      char* kp = smem + kKpeO + (t % kNKpe) * kKpeBytes;
+#pragma unroll
+      for (int j = 0; j < kRawLoads; ++j) {
+        const int c = 2 * j + half;  // 16-column chunk of the lane's key
+        const int cc = j < kCkvDmas / 2 ? c : c - kCkvDmas;
+        const int sw = kSwzB * (cc & 1);
+        char* dst = (j < kCkvDmas / 2 ? stg : kp) + cc * 1024;
+        *reinterpret_cast<u32x4_t*>(dst + ((l32 ^ sw) * 16)) = cvt_fp8x8(r[j][0], r[j][1]);
+        *reinterpret_cast<u32x4_t*>(dst + 512 + ((l32 ^ kSwzA ^ sw) * 16)) = cvt_fp8x8(r[j][2], r[j][3]);
+      }
+    };
+
+    for (int next = w_begin;;) {
+      int it;
+      if (next < w_end) {
+        it = next++;
+      } else {
+        if (pool_n <= 0) break;
+        int* xfer = reinterpret_cast<int*>(smem + kPageOff);
+        if (wave == 0 && lane == 0) *xfer = popped;
+        lds_barrier();
+        const int k = __builtin_amdgcn_readfirstlane(*xfer);
+        if (k >= pool_n) break;
+        it = pool_begin + k;
+      }
+      const bool pre = fast_first && it == w_begin;
+      if (pre) {
+        token = f_token;
+        kv_begin = f_begin;
+        kv_end = f_end;
+        slot = f_slot;
+        page_base = f_base;
+      } else {
+        const_i32_t* item = (const_i32_t*)(a.items) + it * 8;
+        token = item[0];
+        kv_begin = item[2];
+        kv_end = item[3];
+        slot = item[4];
+        page_base = item[5];
+      }
+      const int ntiles = (kv_end - kv_begin + kTileKeys - 1) / kTileKeys;
+
+      f32x16_t o[NW][kDimBlocks];
+      float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
+      for (;;) {
+        if constexpr (!producer) {
+#pragma unroll
+          for (int db = 0; db < kDimBlocks; ++db)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) o[0][db][j] = 0.f;
+        }
+        l_run = 0.f;
+        m_seen = -INFINITY;
+        lds_barrier();  // (both waves are done with the previous item's LDS)
+        if (ntiles == 0) break;
+        if constexpr (producer) {
+          RawTile ra, rb;
+          int n_pages = 1;
+          if (kTileInPage) {
+            const int P = a.page_size;
+            first_page = kv_begin / P;
+            n_pages = (kv_end - 1) / P - first_page + 1;
+            if (!(pre && f_pages)) {
+              const int ln = opaque(lane);
+#pragma unroll
+              for (int k = 0; k < kPageLoads; ++k) {
+                const int i0 = k * kWave;
+                if (i0 < n_pages)
+                  dma4(a.kv_indices + page_base + first_page + min(i0 + ln, n_pages - 1),
+                       lds_base + kPageOff + i0 * 4);
+              }
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          }
+          auto tile_page = [&](int t) {
+            return kTileInPage ? __builtin_amdgcn_readfirstlane(
+                                     page_at((kv_begin + t * kTileKeys) / a.page_size - first_page))
+                               : 0;
+          };
+          // Two register tiles alternate (even tiles in ra, odd in rb), so
+          // that no copy waits for loads in flight; one barrier per tile.
+          raw_load(0, tile_page(0), ra);
+          if (ntiles > 1) raw_load(1, tile_page(1), rb);
+          raw_store(0, ra);
+          lds_barrier();  // tile 0 is in stage 0
+          for (int t = 0; t < ntiles; t += 2) {
+            if (t + 2 < ntiles) raw_load(t + 2, tile_page(t + 2), ra);
+            if (t + 1 < ntiles) raw_store(t + 1, rb);
+            lds_barrier();  // (the computing wave has finished tile t)
+            if (t + 1 >= ntiles) break;
+            if (t + 3 < ntiles) raw_load(t + 3, tile_page(t + 3), rb);
+            if (t + 2 < ntiles) raw_store(t + 2, ra);
+            lds_barrier();  // (... and tile t+1)
+          }
+        } else {
+          u32x4_t q[kQSteps];
+          load_query(H, q);
+#pragma unroll
+          for (int ks = 0; ks < kQSteps; ++ks) asm volatile("" : : "v"(q[ks]));
+          lds_barrier();  // tile 0 is in stage 0
+          for (int t = 0; t < ntiles; ++t) {
+            const int base = kv_begin + t * kTileKeys;
+            float x[16];
+            scores(stage(t), kpe_slot(t), q, x, [&](auto) {});
+            bf16x8_t p[2];
+            const float mx = softmax_max(x, base, m_seen);
+            if (t == 0) {
+              const float mh = fmaxf(mx, __shfl_xor(mx, 32));
+              if (m_ref == -INFINITY) m_ref = mh;  // O is still zero
+            }
+            softmax_exp<0, 16>(x, -m_ref, l_run, p);
+            store_p(p, pbuf(t));
+            pv(stage(t), pbuf(t), o, [&](auto) {});
+            lds_barrier();  // (tile t's stage is free; tile t+1 is in the other)
+          }
+        }
+        // Redo the item if a head overflowed its reference (decided by the
+        // computing wave, read by both).
+        int* flags = reinterpret_cast<int*>(smem + kFlagOff);
+        if constexpr (!producer) {
+          const bool redo = __any(m_seen > m_ref + kMaxExponent);
+          if (lane == 0) flags[0] = redo ? 1 : 0;
+        }
+        lds_barrier();
+        const int any_redo = __builtin_amdgcn_readfirstlane(flags[0]);
+        if (!any_redo) break;
+        m_ref = fmaxf(m_seen, __shfl_xor(m_seen, 32));
+        lds_barrier();  // (the flag is read before the next attempt's barrier reuses the slot)
+      }
+      if (pool_n > 0 && next >= w_end) pop();
+      if constexpr (producer)
+        lds_barrier();  // (the one barrier of the finish)
+      else
+        finish(o, m_ref, l_run);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    if (pool_n > 0 && wave == 0 && lane == 0) {
+      const int d = __hip_atomic_fetch_add(a.pool_ctr + 1, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      if (d == static_cast<int>(gridDim.x) - 1) {
+        __hip_atomic_store(a.pool_ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.pool_ctr + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    if (a.done_flags && wave == 0 && lane == 0)
+      __hip_atomic_store(a.done_flags + blockIdx.x, a.run_seq, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+
   __device__ __forceinline__ void store_p(const bf16x8_t (&p)[2], char* pb) const {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -1147,6 +1382,16 @@ void attention_kernel(AttnArgs args) {
   k.run();
 }
 
+// fp8 cache, at most 32 heads, two workgroups per compute unit: a computing
+// and a producing wave per workgroup (Attn::run_split).
+template <bool kTileInPage>
+__global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attention_split_kernel(AttnArgs args) {
+  __shared__ __attribute__((aligned(1024))) char smem[Attn<1, kTileInPage, false, true>::kLdsBytes];
+  Attn<1, kTileInPage, false, true> k(args, smem);
+  k.run_split();
+}
+
 template <int NW, bool kFp8, bool kCompact = false>
 hipError_t launch_nw(const AttnArgs& a, int num_workers, hipStream_t stream) {
   if (a.page_size % kTileKeys == 0)
@@ -1161,7 +1406,17 @@ hipError_t launch_nw(const AttnArgs& a, int num_workers, hipStream_t stream) {
 template <bool kFp8>
 hipError_t launch_dtype(const AttnArgs& a, int num_workers, hipStream_t stream) {
   if (a.num_heads <= 32) {
-    if (a.compact) return launch_nw<1, kFp8, true>(a, num_workers, stream);
+    if (a.compact && kFp8) {
+      if (a.page_size % kTileKeys == 0)
+        hipLaunchKernelGGL(attention_split_kernel<true>, dim3(num_workers), dim3(2 * kWave), 0,
+                           stream, a);
+      else
+        hipLaunchKernelGGL(attention_split_kernel<false>, dim3(num_workers), dim3(2 * kWave), 0,
+                           stream, a);
+      return hipGetLastError();
+    }
+    if constexpr (!kFp8)
+      if (a.compact) return launch_nw<1, false, true>(a, num_workers, stream);
     return launch_nw<1, kFp8>(a, num_workers, stream);
   }
   if (a.num_heads <= 64) return launch_nw<2, kFp8>(a, num_workers, stream);
