@@ -2,8 +2,8 @@
 mla_append_kv_fp8), against the fp64 oracle: ragged batches over every
 kernel variant (one, two and four waves; tiles inside pages and per-key
 pages), the full decode and long-decode batches, the overflow-redo path,
-a batch with a shared pool of whole-token items, and the quantising append
-bit for bit."""
+a batch with a shared pool of whole-token items, HIP-graph replays, and the
+quantising append bit for bit."""
 
 import numpy as np
 import pytest
@@ -190,5 +190,61 @@ def test_fp8_shared_pool_every_token(heads, page_size):
             o, lse = _run_fp8(w, codes, scale, plan=plan)
             o_ref, l_ref = _oracle_fp8(w, codes, scale)
             assert_close(o, lse, o_ref, l_ref, f"fp8 shared pool H={heads} P={page_size} run {rep}")
+    finally:
+        plan.close()
+
+
+@pytest.mark.parametrize("heads,page_size,shape", [(16, 64, "decode"), (32, 16, "pool"),
+                                                   (128, 64, "decode")])
+def test_fp8_graph_replays_match_eager(heads, page_size, shape):
+    """mla_run_fp8 captured in a HIP graph and replayed, with eager runs
+    between the replays: every replay equals the eager result bit for bit
+    (the two-wave split kernel up to 32 heads, from the host slot and with a
+    shared pool; the four-wave kernel at 128 heads)."""
+    import paged_mla_attention_amd as pm
+    rng = np.random.default_rng(520 + heads + page_size)
+    if shape == "decode":
+        w = W.make_workload("fp8_g", 0, [700, 33, 1500, 64, 2100], [1] * 5, heads, page_size,
+                            rng=rng)
+    else:
+        workers = torch.cuda.get_device_properties(0).multi_processor_count * 2
+        q_len = (4 * workers + 7) // 8 + 3
+        kv = q_len + np.array([0, 1200, 40, 1500, 10, 900, 0, 1300])
+        w = W.make_workload("fp8_gp", 0, kv, [q_len] * 8, heads, page_size, rng=rng)
+    scale = 0.11
+    codes = torch.from_numpy(np.ascontiguousarray(W.fp8_cache_codes(w.kv_cache, scale))).cuda()
+    qn, qp = _dev_bits(w.q_nope), _dev_bits(w.q_pe)
+    T, H = w.num_tokens, heads
+    plan = pm.MLAPlan(H, page_size)
+    try:
+        plan.plan(w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_len, causal=True,
+                  sm_scale=w.sm_scale, num_cache_pages=w.num_pages, kv_dtype="fp8_e4m3")
+        out = torch.empty((T, H, 512), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((T, H), dtype=torch.float32, device="cuda")
+        plan.run(qn, qp, codes, out=out, lse=lse, kv_scale=scale)
+        torch.cuda.synchronize()
+        ref_o, ref_l = out.clone(), lse.clone()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            plan.run(qn, qp, codes, out=out, lse=lse, stream=st, kv_scale=scale)
+        torch.cuda.current_stream().wait_stream(st)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            plan.run(qn, qp, codes, out=out, lse=lse, kv_scale=scale)
+        for k in range(3):
+            out.fill_(0)
+            lse.fill_(0)
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref_o), f"replay {k}: output differs"
+            assert torch.equal(lse, ref_l), f"replay {k}: lse differs"
+            plan.run(qn, qp, codes, out=out, lse=lse, kv_scale=scale)
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref_o)
+        o_ref, l_ref = _oracle_fp8(w, W.fp8_cache_codes(w.kv_cache, scale), scale)
+        assert_close(from_dev_bf16(ref_o), ref_l.cpu().numpy(), o_ref, l_ref,
+                     f"fp8 graph H={heads} P={page_size}")
     finally:
         plan.close()
