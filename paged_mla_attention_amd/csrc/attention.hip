@@ -623,6 +623,50 @@ struct Attn {
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   }
 
+  // The workgroup's start, read with one lane-parallel load: from the host
+  // slot (fast_first) the first item with the worker's item range in two of
+  // its fields (32 bytes, no shared pool there); otherwise the worker's item
+  // range (lanes 8, 9) and the shared pool's (lanes 10, 11) from
+  // worker_indptr.
+  struct Entry {
+    int f_token, f_begin, f_end, f_slot, f_base, f_pages;
+    int w_begin, w_end, pool_begin, pool_n;
+  };
+  __device__ __forceinline__ Entry read_entry(bool fast_first) const {
+    int v = 0;
+    {
+      const int l = opaque(lane);
+      const int* src = nullptr;
+      if (fast_first) {
+        if (l < 8) src = reinterpret_cast<const int*>(a.first_items) + blockIdx.x * 8 + l;
+      } else if (l == 8 || l == 9) {
+        src = a.worker_indptr + blockIdx.x + (l - 8);
+      } else if (l == 10 || l == 11) {
+        src = a.worker_indptr + gridDim.x + (l - 10);
+      }
+      if (src) v = *src;
+    }
+    Entry e;
+    e.f_token = __builtin_amdgcn_readlane(v, 0);
+    e.f_begin = __builtin_amdgcn_readlane(v, 2);
+    e.f_end = __builtin_amdgcn_readlane(v, 3);
+    e.f_slot = __builtin_amdgcn_readlane(v, 4);
+    e.f_base = __builtin_amdgcn_readlane(v, 5);
+    e.f_pages = __builtin_amdgcn_readlane(v, 7);  // (pad[1]: the page list is staged)
+    if (fast_first) {
+      e.w_begin = __builtin_amdgcn_readlane(v, 1);  // (row field)
+      e.w_end = __builtin_amdgcn_readlane(v, 6);    // (pad[0])
+      e.pool_begin = 0;
+      e.pool_n = 0;
+    } else {
+      e.w_begin = __builtin_amdgcn_readlane(v, 8);
+      e.w_end = __builtin_amdgcn_readlane(v, 9);
+      e.pool_begin = __builtin_amdgcn_readlane(v, 10);
+      e.pool_n = __builtin_amdgcn_readlane(v, 11) - e.pool_begin;
+    }
+    return e;
+  }
+
   __device__ void run() {
     // A schedule in the host slot: the first item is read straight from
     // first_items (no dependent worker_indptr read) and, where it was staged,
@@ -631,30 +675,9 @@ struct Attn {
     // one lane-parallel load: lanes 0..7 the item's fields, lanes 8 and 9
     // this worker's item range, lanes 10 and 11 the shared pool's.
     const bool fast_first = kTileInPage && a.first_items != nullptr;
-    if (fast_first && wave == 0)
+    if (fast_first && wave == 0 && lane < kFirstPages)
       dma4(a.first_pages + blockIdx.x * kFirstPages + lane, lds_base + kPageOff);
-    int entry = 0;
-    {
-      const int l = opaque(lane);
-      const int* src = nullptr;
-      if (l < 8 && fast_first)
-        src = reinterpret_cast<const int*>(a.first_items) + blockIdx.x * 8 + l;
-      else if (l == 8 || l == 9)
-        src = a.worker_indptr + blockIdx.x + (l - 8);
-      else if (l == 10 || l == 11)
-        src = a.worker_indptr + gridDim.x + (l - 10);
-      if (src) entry = *src;
-    }
-    const int f_token = __builtin_amdgcn_readlane(entry, 0);
-    const int f_begin = __builtin_amdgcn_readlane(entry, 2);
-    const int f_end = __builtin_amdgcn_readlane(entry, 3);
-    const int f_slot = __builtin_amdgcn_readlane(entry, 4);
-    const int f_base = __builtin_amdgcn_readlane(entry, 5);
-    const int f_pages = __builtin_amdgcn_readlane(entry, 7);  // (pad[1]: the page list is staged)
-    const int w_begin = __builtin_amdgcn_readlane(entry, 8);
-    const int w_end = __builtin_amdgcn_readlane(entry, 9);
-    const int pool_begin = __builtin_amdgcn_readlane(entry, 10);
-    const int pool_n = __builtin_amdgcn_readlane(entry, 11) - pool_begin;
+    const Entry e = read_entry(fast_first);
     const int H = a.num_heads;
 
     // The shared pool (a schedule with many query tokens): once its own
@@ -669,31 +692,31 @@ struct Attn {
       if (wave == 0 && lane == 0)
         popped = __hip_atomic_fetch_add(a.pool_ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
-    if (pool_n > 0 && w_begin == w_end) pop();
+    if (e.pool_n > 0 && e.w_begin == e.w_end) pop();
 
-    for (int next = w_begin;;) {
+    for (int next = e.w_begin;;) {
       int it;
-      if (next < w_end) {
+      if (next < e.w_end) {
         it = next++;
       } else {
-        if (pool_n <= 0) break;
+        if (e.pool_n <= 0) break;
         // (the page-list area: no wave reads it until after the item's
         // first barrier, and its DMA is issued after that barrier)
         int* xfer = reinterpret_cast<int*>(smem + kPageOff);
         if (wave == 0 && lane == 0) *xfer = popped;
         lds_barrier();
         const int k = __builtin_amdgcn_readfirstlane(*xfer);
-        if (k >= pool_n) break;
-        it = pool_begin + k;
+        if (k >= e.pool_n) break;
+        it = e.pool_begin + k;
       }
       // (the first item of a host-slot schedule was read at entry)
-      const bool pre = fast_first && it == w_begin;
+      const bool pre = fast_first && it == e.w_begin;
       if (pre) {
-        token = f_token;
-        kv_begin = f_begin;
-        kv_end = f_end;
-        slot = f_slot;
-        page_base = f_base;
+        token = e.f_token;
+        kv_begin = e.f_begin;
+        kv_end = e.f_end;
+        slot = e.f_slot;
+        page_base = e.f_base;
       } else {
         const_i32_t* item = (const_i32_t*)(a.items) + it * 8;  // WorkItem fields
         token = item[0];
@@ -737,7 +760,7 @@ struct Attn {
           const int P = a.page_size;
           first_page = kv_begin / P;
           n_pages = (kv_end - 1) / P - first_page + 1;  // <= kMaxItemTiles
-          if (!(pre && f_pages)) stage_pages(n_pages);  // (else DMA'd at entry)
+          if (!(pre && e.f_pages)) stage_pages(n_pages);  // (else DMA'd at entry)
         } else {
 #pragma unroll
           for (int t = 0; t < kIdAhead; ++t)
@@ -894,7 +917,7 @@ struct Attn {
         if (!any_redo) break;
         m_ref = fmaxf(m_seen, __shfl_xor(m_seen, 32));  // the head's largest score
       }
-      if (pool_n > 0 && next >= w_end) pop();  // the next item comes from the pool
+      if (e.pool_n > 0 && next >= e.w_end) pop();  // the next item comes from the pool
       finish(o, m_ref, l_run);
     }
     // Every read of the schedule (items, page lists) has been consumed by
@@ -902,7 +925,7 @@ struct Attn {
     // tell the host this workgroup is done with the slot.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
-    if (pool_n > 0 && wave == 0 && lane == 0) {
+    if (e.pool_n > 0 && wave == 0 && lane == 0) {
       // This workgroup has drawn past the pool's end; the last one to do so
       // leaves the counters at zero for the next run (every draw of every
       // workgroup has returned by then).
@@ -938,30 +961,9 @@ struct Attn {
   template <bool producer>
   __device__ __forceinline__ void split_loop() {
     const bool fast_first = kTileInPage && a.first_items != nullptr;
-    if (fast_first && producer)
+    if (fast_first && producer && lane < kFirstPages)
       dma4(a.first_pages + blockIdx.x * kFirstPages + lane, lds_base + kPageOff);
-    int entry = 0;
-    {
-      const int l = opaque(lane);
-      const int* src = nullptr;
-      if (l < 8 && fast_first)
-        src = reinterpret_cast<const int*>(a.first_items) + blockIdx.x * 8 + l;
-      else if (l == 8 || l == 9)
-        src = a.worker_indptr + blockIdx.x + (l - 8);
-      else if (l == 10 || l == 11)
-        src = a.worker_indptr + gridDim.x + (l - 10);
-      if (src) entry = *src;
-    }
-    const int f_token = __builtin_amdgcn_readlane(entry, 0);
-    const int f_begin = __builtin_amdgcn_readlane(entry, 2);
-    const int f_end = __builtin_amdgcn_readlane(entry, 3);
-    const int f_slot = __builtin_amdgcn_readlane(entry, 4);
-    const int f_base = __builtin_amdgcn_readlane(entry, 5);
-    const int f_pages = __builtin_amdgcn_readlane(entry, 7);
-    const int w_begin = __builtin_amdgcn_readlane(entry, 8);
-    const int w_end = __builtin_amdgcn_readlane(entry, 9);
-    const int pool_begin = __builtin_amdgcn_readlane(entry, 10);
-    const int pool_n = __builtin_amdgcn_readlane(entry, 11) - pool_begin;
+    const Entry e = read_entry(fast_first);
     const int H = a.num_heads;
 
     // (the shared pool as in run(): the computing wave draws, through LDS)
@@ -970,7 +972,7 @@ struct Attn {
       if (wave == 0 && lane == 0)
         popped = __hip_atomic_fetch_add(a.pool_ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
-    if (pool_n > 0 && w_begin == w_end) pop();
+    if (e.pool_n > 0 && e.w_begin == e.w_end) pop();
 
     // Producer: this lane's key of a tile and which 16-column chunks of it
     // (c = 2 j + half, j = 0 .. 17) it converts.
@@ -1004,26 +1006,26 @@ struct Attn {
       }
     };
 
-    for (int next = w_begin;;) {
+    for (int next = e.w_begin;;) {
       int it;
-      if (next < w_end) {
+      if (next < e.w_end) {
         it = next++;
       } else {
-        if (pool_n <= 0) break;
+        if (e.pool_n <= 0) break;
         int* xfer = reinterpret_cast<int*>(smem + kPageOff);
         if (wave == 0 && lane == 0) *xfer = popped;
         lds_barrier();
         const int k = __builtin_amdgcn_readfirstlane(*xfer);
-        if (k >= pool_n) break;
-        it = pool_begin + k;
+        if (k >= e.pool_n) break;
+        it = e.pool_begin + k;
       }
-      const bool pre = fast_first && it == w_begin;
+      const bool pre = fast_first && it == e.w_begin;
       if (pre) {
-        token = f_token;
-        kv_begin = f_begin;
-        kv_end = f_end;
-        slot = f_slot;
-        page_base = f_base;
+        token = e.f_token;
+        kv_begin = e.f_begin;
+        kv_end = e.f_end;
+        slot = e.f_slot;
+        page_base = e.f_base;
       } else {
         const_i32_t* item = (const_i32_t*)(a.items) + it * 8;
         token = item[0];
@@ -1054,7 +1056,7 @@ struct Attn {
             const int P = a.page_size;
             first_page = kv_begin / P;
             n_pages = (kv_end - 1) / P - first_page + 1;
-            if (!(pre && f_pages)) {
+            if (!(pre && e.f_pages)) {
               const int ln = opaque(lane);
 #pragma unroll
               for (int k = 0; k < kPageLoads; ++k) {
@@ -1121,7 +1123,7 @@ struct Attn {
         m_ref = fmaxf(m_seen, __shfl_xor(m_seen, 32));
         lds_barrier();  // (the flag is read before the next attempt's barrier reuses the slot)
       }
-      if (pool_n > 0 && next >= w_end) pop();
+      if (e.pool_n > 0 && next >= e.w_end) pop();
       if constexpr (producer)
         lds_barrier();  // (the one barrier of the finish)
       else
@@ -1129,7 +1131,7 @@ struct Attn {
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
-    if (pool_n > 0 && wave == 0 && lane == 0) {
+    if (e.pool_n > 0 && wave == 0 && lane == 0) {
       const int d = __hip_atomic_fetch_add(a.pool_ctr + 1, 1, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
       if (d == static_cast<int>(gridDim.x) - 1) {

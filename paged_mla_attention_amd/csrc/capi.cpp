@@ -437,14 +437,18 @@ mla_status mla_plan(mla_plan_t p, const int32_t* qo_indptr, const int32_t* kv_in
     auto* fp = reinterpret_cast<int32_t*>(h + off_fpages);
     for (int w = 0; w < s.num_workers; ++w) {
       int32_t* pages = fp + static_cast<size_t>(w) * mla::kFirstPages;
-      if (s.worker_indptr[w] == s.worker_indptr[w + 1]) {
-        fi[w] = mla::WorkItem{0, 0, 0, 0, -1, 0, {0, 0}};
+      const int32_t wb = s.worker_indptr[w], we = s.worker_indptr[w + 1];
+      if (wb == we) {
+        fi[w] = mla::WorkItem{0, wb, 0, 0, -1, 0, {we, 0}};
         std::memset(pages, 0, mla::kFirstPages * sizeof(int32_t));
         continue;
       }
-      mla::WorkItem it = s.items[s.worker_indptr[w]];
-      // The item's pages; entries past its last page repeat it (the kernel
-      // never reads them).  pad[1] = 1: the list is staged.
+      mla::WorkItem it = s.items[wb];
+      // The worker's item range rides in the fields the kernel does not read
+      // (row, pad[0]).  The item's pages; entries past its last page repeat
+      // it (the kernel never reads them).  pad[1] = 1: the list is staged.
+      it.row = wb;
+      it.pad[0] = we;
       const int32_t first_page = it.kv_end > it.kv_begin ? it.kv_begin / p->page_size : 0;
       const int32_t n_pages =
           it.kv_end > it.kv_begin ? (it.kv_end - 1) / p->page_size - first_page + 1 : 0;

@@ -43,9 +43,11 @@ struct AttnArgs {
   // Schedule read from a pinned host slot: each workgroup stores run_seq to
   // done_flags[workgroup] once it has read the slot for the last time (the
   // host waits on these before refilling it).  first_items[w] is worker w's
-  // first item (indexed directly, without worker_indptr), and, when its
-  // first_pages flag (the item's last field) is set, its page list is
-  // first_pages[w * kFirstPages ...], copied to LDS at kernel entry.
+  // first item with its item range in the fields the kernel does not read
+  // ({token, w_begin, kv_begin, kv_end, slot, page_base, w_end, staged}), so
+  // that one 32-byte read starts the workgroup; when staged is set, the
+  // item's page list is first_pages[w * kFirstPages ...], copied to LDS at
+  // kernel entry.  Such a schedule has no shared pool.
   int32_t* done_flags;
   int32_t run_seq;
   const WorkItem* first_items;
@@ -63,7 +65,7 @@ struct AppendRows {
 };
 
 // Pages of a worker's first item staged per worker in the host slot.
-constexpr int kFirstPages = 64;
+constexpr int kFirstPages = 16;
 // Merge entries handed to the merge kernel as kernel arguments (schedules
 // read from the host slot).
 constexpr int kInlineMerges = 192;
