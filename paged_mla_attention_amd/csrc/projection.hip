@@ -113,9 +113,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void h
   // Row-piece task of a lane: token 4 j + lane / 16 of the wave's 32 (j = 0..7),
   // columns 8 (lane % 16) .. + 7 of the piece.
   const int pr = lane >> 4, pc = 8 * (lane & 15);
+  // Up-projection input pieces: piece c (columns 128 c .. + 127) of this
+  // wave's 32 tokens of a block, 8 loads of 16 bytes per lane.  All K / 128
+  // pieces of the next block are in flight while this block's are used:
+  // piece c of block b+1 is loaded as soon as piece c of block b has gone to
+  // LDS.
+  constexpr int kPieces = S::kStageOut ? 1 : K / kChunk;
+  u32x4_t buf[kPieces][8];
+  auto load_piece = [&](int64_t tw, int c, u32x4_t (&v)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      int64_t t = tw + 4 * j + pr;
+      t = t < T ? t : T - 1;
+      v[j] = *reinterpret_cast<const u32x4_t*>(x + (t * H + h) * K + c * kChunk + pc);
+    }
+  };
+  if constexpr (!S::kStageOut) {
+    const int64_t tw0 = static_cast<int64_t>(bx) * kTok + 32 * wave;
+    if (tw0 < T)
+#pragma unroll
+      for (int c = 0; c < kPieces; ++c) load_piece(tw0, c, buf[c]);
+  }
   for (int64_t t0 = static_cast<int64_t>(bx) * kTok; t0 < T; t0 += static_cast<int64_t>(n_bx) * kTok) {
     const int64_t tw = t0 + 32 * wave;
     if (tw >= T) break;
+    const int64_t tw_next = tw + static_cast<int64_t>(n_bx) * kTok;
     f32x16_t acc[S::kNBlocks];
 #pragma unroll
     for (int nb = 0; nb < S::kNBlocks; ++nb)
@@ -142,24 +164,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void h
       for (int ks = 0; ks < S::kKSteps; ++ks) mfma_step(ks, xb[ks]);
     } else {
       // The input rows arrive in 128-column pieces, 256 bytes per token per
-      // load, through LDS; the next piece's loads go out before this one's
-      // MFMAs.
-      auto load_piece = [&](int c, u32x4_t (&v)[8]) {
+      // load, through LDS (buf holds this block's pieces, loaded during the
+      // previous block).
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          int64_t t = tw + 4 * j + pr;
-          t = t < T ? t : T - 1;
-          v[j] = *reinterpret_cast<const u32x4_t*>(x + (t * H + h) * K + c * kChunk + pc);
-        }
-      };
-      u32x4_t cur[8], nxt[8];
-      load_piece(0, cur);
-#pragma unroll
-      for (int c = 0; c < K / kChunk; ++c) {
-        if (c + 1 < K / kChunk) load_piece(c + 1, nxt);
+      for (int c = 0; c < kPieces; ++c) {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-          *reinterpret_cast<u32x4_t*>(piece + ((4 * j + pr) * kPieceRow + pc) * 2) = cur[j];
+          *reinterpret_cast<u32x4_t*>(piece + ((4 * j + pr) * kPieceRow + pc) * 2) = buf[c][j];
+        if (tw_next < T) load_piece(tw_next, c, buf[c]);
         wave_lds_sync();
 #pragma unroll
         for (int kk = 0; kk < kChunk / 16; ++kk) {
@@ -168,8 +180,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void h
           mfma_step(c * (kChunk / 16) + kk, xv);
         }
         wave_lds_sync();  // (the piece is rewritten next)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) cur[j] = nxt[j];
       }
     }
     // acc[nb][4 i + j] is out^T[n, t] for column n = 32 nb + 8 i + 4 half + j
