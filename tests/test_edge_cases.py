@@ -153,3 +153,25 @@ def test_shared_pool_every_token_and_counter_reset(heads, page_size):
             assert_close(o, lse, o_ref, l_ref, f"shared pool H={heads} P={page_size} run {rep}")
     finally:
         plan.close()
+
+
+@pytest.mark.parametrize("heads,rows,keys", [(128, 8, 20000), (16, 8, 40000)])
+def test_host_slot_first_items_beyond_staged_pages(heads, rows, keys):
+    """A decode batch small enough for the pinned host slot whose first items
+    span more pages than the slot stages per worker (page size 32, about 20
+    pages each): those workgroups load the page list from the slot's copy of
+    the page table instead.  Every token against the oracle."""
+    import paged_mla_attention_amd as pm
+    rng = np.random.default_rng(61 + heads)
+    w = W.make_workload("hs_pages", 0, [keys] * rows, [1] * rows, heads, 32, rng=rng)
+    workers = torch.cuda.get_device_properties(0).multi_processor_count * (2 if heads <= 32 else 1)
+    s = pm.schedule(w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_len, 32, w.num_pages,
+                    heads, workers)
+    it, wi = s["items"], s["worker_indptr"]
+    assert len(it) <= 2 * workers and len(s["merges"]) <= 192  # (read from the host slot)
+    pages = [(it[wi[k]][3] - 1) // 32 - it[wi[k]][2] // 32 + 1
+             for k in range(workers) if wi[k + 1] > wi[k]]
+    assert max(pages) > 16
+    o, lse = run_library(w)
+    o_ref, l_ref = oracle_of(w)
+    assert_close(o, lse, o_ref, l_ref, f"host slot, first items beyond staged pages, H={heads}")

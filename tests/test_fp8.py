@@ -248,3 +248,16 @@ def test_fp8_graph_replays_match_eager(heads, page_size, shape):
                      f"fp8 graph H={heads} P={page_size}")
     finally:
         plan.close()
+
+
+def test_fp8_host_slot_first_items_beyond_staged_pages():
+    """The two-wave fp8 kernel on a host-slot schedule whose first items span
+    about 20 pages (more than the slot stages per worker): the producer wave
+    loads those page lists from the slot's page table."""
+    rng = np.random.default_rng(611)
+    w = W.make_workload("fp8_hs_pages", 0, [40000] * 8, [1] * 8, 16, 32, rng=rng)
+    scale = 0.07
+    codes = W.fp8_cache_codes(w.kv_cache, scale)
+    o, lse = _run_fp8(w, codes, scale)
+    o_ref, l_ref = _oracle_fp8(w, codes, scale)
+    assert_close(o, lse, o_ref, l_ref, "fp8 host slot, first items beyond staged pages")
