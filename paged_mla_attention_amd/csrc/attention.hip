@@ -51,6 +51,10 @@
 //   * the query rows are loaded and waited for before the item's first DMA,
 //     and page ids come from LDS, so nothing inside the key loop makes the
 //     in-order vmcnt drain the DMA queue;
+//   * at most 32 heads (one computing wave), two workgroups share a compute
+//     unit in 80 KiB of LDS each; with an fp8 cache each of them adds a
+//     producer wave on an otherwise idle SIMD that loads and converts the
+//     codes while the computing wave runs the products (run_split);
 //   * items covering a token's whole key range write bf16 output + LSE;
 //     pieces of a split token write normalised bf16 partials and their LSE,
 //     which a merge kernel combines.

@@ -35,9 +35,10 @@ struct AttnArgs {
   // reads unscaled: it multiplies the scores (with scale_log2) and the
   // normalised output.
   float out_scale;
-  // One-wave kernels (at most 32 heads): nonzero selects the compact
-  // variant that runs two workgroups per compute unit; the schedule must
-  // then have been made for two workers per compute unit.
+  // At most 32 heads: nonzero selects the compact kernels that run two
+  // workgroups per compute unit (one wave each; with an fp8 cache a
+  // computing and a producing wave each); the schedule must then have been
+  // made for two workers per compute unit.
   int32_t compact;
   const float* scale_log2_ptr;  // non-null: read the scale here (reserved plans)
   // Schedule read from a pinned host slot: each workgroup stores run_seq to
