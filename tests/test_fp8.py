@@ -50,7 +50,7 @@ def _oracle_fp8(w, codes, scale, tokens=None):
                                 tokens=tokens)
 
 
-@pytest.mark.parametrize("heads", [16, 32, 64, 128])
+@pytest.mark.parametrize("heads", [1, 16, 24, 32, 40, 64, 100, 128])
 @pytest.mark.parametrize("page_size", [1, 16, 33, 64])
 def test_fp8_ragged_small(heads, page_size):
     rng = np.random.default_rng(300 + heads + page_size)

@@ -44,7 +44,7 @@ def test_tiny_golden_fixture():
     assert np.abs(lse - np.array(doc["lse"])).max() <= 2e-3
 
 
-@pytest.mark.parametrize("heads", [16, 32, 40, 64, 128])
+@pytest.mark.parametrize("heads", [1, 16, 24, 32, 40, 64, 100, 128])
 @pytest.mark.parametrize("page_size", [1, 16, 33, 64])
 def test_ragged_small(heads, page_size):
     """Ragged rows spanning several 32-key tiles with ragged tails, a row
