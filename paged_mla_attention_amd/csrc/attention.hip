@@ -1412,7 +1412,8 @@ hipError_t launch_nw(const AttnArgs& a, int num_workers, hipStream_t stream) {
 template <bool kFp8>
 hipError_t launch_dtype(const AttnArgs& a, int num_workers, hipStream_t stream) {
   if (a.num_heads <= 32) {
-    if (a.compact && kFp8) {
+    if constexpr (kFp8) {
+      // (any worker count; the planner gives it two per compute unit)
       if (a.page_size % kTileKeys == 0)
         hipLaunchKernelGGL(attention_split_kernel<true>, dim3(num_workers), dim3(2 * kWave), 0,
                            stream, a);
@@ -1420,10 +1421,10 @@ hipError_t launch_dtype(const AttnArgs& a, int num_workers, hipStream_t stream) 
         hipLaunchKernelGGL(attention_split_kernel<false>, dim3(num_workers), dim3(2 * kWave), 0,
                            stream, a);
       return hipGetLastError();
-    }
-    if constexpr (!kFp8)
+    } else {
       if (a.compact) return launch_nw<1, false, true>(a, num_workers, stream);
-    return launch_nw<1, kFp8>(a, num_workers, stream);
+      return launch_nw<1, false>(a, num_workers, stream);
+    }
   }
   if (a.num_heads <= 64) return launch_nw<2, kFp8>(a, num_workers, stream);
   return launch_nw<4, kFp8>(a, num_workers, stream);
