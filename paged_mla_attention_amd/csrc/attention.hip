@@ -837,6 +837,7 @@ struct Attn {
           const bool dma = t + kAhead < ntiles;
           const int base = kv_begin + t * kTileKeys;
           float x[16];
+          PvOps pvo;  // operands of this wave's first P . V step (several waves)
           {
             TileDma d{};  // (defined on every path: a phi with undef would put it in VGPRs)
             auto prep = [&] {
@@ -854,14 +855,23 @@ struct Attn {
             // registers to spare there).  The DMAs go under the other
             // k-steps.
             constexpr bool kPrepUnder = NW > 1;
-            // (the DMA test at every k-step is a scalar branch on this
-            // wave-uniform value; as a plain bool it was rebuilt by VALU
-            // instructions on the path of each DMA)
+            // (the DMA test at every k-step is a scalar compare and branch
+            // on this wave-uniform value, re-read from an opaque SGPR copy:
+            // a condition the compiler keeps live across the k-steps becomes
+            // a lane mask, rebuilt by VALU instructions in front of each DMA)
             const int dma_s = __builtin_amdgcn_readfirstlane(dma ? 1 : 0);
             if (!kPrepUnder && dma_s) prep();
             scores(stage(t), kpe_slot(t), q, x, [&](auto kc) {
               constexpr int k = decltype(kc)::value;
-              if (!dma_s) return;
+              // The first P . V operands of tile t-1 (published before this
+              // iteration's barrier) go out under the chain's last k-steps,
+              // so the P . V chain starts without an LDS round trip.
+              if constexpr (kPipe && k == kQSteps - 3) {
+                if (t > 0) pv_load(stage(t - 1), pbuf(t - 1), pvo);
+              }
+              int dsv = __builtin_amdgcn_readfirstlane(dma_s);
+              asm volatile("" : "+s"(dsv));
+              if (!dsv) return;
               if constexpr (k == 0) {
                 if (kPrepUnder) prep();
               } else {
@@ -879,9 +889,13 @@ struct Attn {
             softmax_exp<0, 16>(x, -m_ref, l_run, p);
           } else {
             const float neg_ref = -m_ref;
-            pv(stage(t - 1), pbuf(t - 1), o, [&](auto sc) {
+            // The softmax goes under the P . V MFMAs one piece per MFMA
+            // (a piece issued after an MFMA runs while that MFMA does; the
+            // next MFMA waits for the pipe anyway): the maximum under the
+            // first, then about one probability per MFMA.
+            pv_run(stage(t - 1), pbuf(t - 1), o, pvo, [&](auto sc) {
               constexpr int st = decltype(sc)::value;
-              constexpr int kN = 2 * kDimBlocks - 1;  // P . V steps after the first
+              constexpr int kN = 2 * kDimBlocks * NW - 1;  // P . V MFMAs after the first
               if constexpr (st == 0) {
                 softmax_max(x, base, m_seen);
               } else {
@@ -1247,47 +1261,66 @@ struct Attn {
   // head slot in P buffer Pb: this wave's 32-column blocks
   // [w kDimBlocks, (w+1) kDimBlocks) times each head group's P^T.
   // Consecutive MFMAs go to different accumulators; V^T operands are read
-  // kAhead column blocks early.
+  // kPvAhead column blocks early.  pv_load issues the first operand reads
+  // (every head group's P^T for the first key half, the first V^T blocks),
+  // which the caller may place earlier; pv_run is the MFMA chain, with
+  // extra(i) placed under its i-th MFMA.
+  static constexpr int kPvAhead = 2;
+  struct PvOps {
+    bf16x8_t pb[NW];
+    bf16x8_t vbuf[kPvAhead];
+  };
+  __device__ __forceinline__ bf16x8_t pv_vload(const char* V, int st) const {
+    // column block st % kDimBlocks, key half st / kDimBlocks
+    const char* kv0 = V + pv_off0 + wave * kDimBlocks * 2048;
+    const char* kv1 = V + pv_off1 + wave * kDimBlocks * 2048;
+    const int off = (st % kDimBlocks) * 2048 + (st / kDimBlocks) * 256;
+    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(kv0 + off));
+    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(kv1 + off));
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+  __device__ __forceinline__ bf16x8_t pv_pload(const char* Pb, int g, int ks) const {
+    return *reinterpret_cast<const bf16x8_t*>(Pb + g * kPGroupBytes + ks * (kWave * 16) + lane * 16);
+  }
+  __device__ __forceinline__ void pv_load(const char* V, const char* Pb, PvOps& ops) const {
+#pragma unroll
+    for (int g = 0; g < NW; ++g) ops.pb[g] = pv_pload(Pb, g, 0);
+#pragma unroll
+    for (int i = 0; i < kPvAhead; ++i) ops.vbuf[i] = pv_vload(V, i);
+  }
   template <typename Extra>
   __device__ __forceinline__ void pv(const char* V, const char* Pb, f32x16_t (&o)[NW][kDimBlocks],
                                      Extra&& extra) const {
+    PvOps ops;
+    pv_load(V, Pb, ops);
+    pv_run(V, Pb, o, ops, extra);
+  }
+  template <typename Extra>
+  __device__ __forceinline__ void pv_run(const char* V, const char* Pb, f32x16_t (&o)[NW][kDimBlocks],
+                                         PvOps& ops, Extra&& extra) const {
     constexpr int kSteps = 2 * kDimBlocks;  // (key half, column block)
-    constexpr int kAhead = 2;
-    const char* kv0 = V + pv_off0 + wave * kDimBlocks * 2048;
-    const char* kv1 = V + pv_off1 + wave * kDimBlocks * 2048;
-    auto vload = [&](int st) {  // column block st % kDimBlocks, key half st / kDimBlocks
-      const int off = (st % kDimBlocks) * 2048 + (st / kDimBlocks) * 256;
-      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(kv0 + off));
-      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(kv1 + off));
-      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    auto pload = [&](int g, int ks) {
-      return *reinterpret_cast<const bf16x8_t*>(Pb + g * kPGroupBytes + ks * (kWave * 16) +
-                                                lane * 16);
-    };
-    bf16x8_t pb[NW];
-#pragma unroll
-    for (int g = 0; g < NW; ++g) pb[g] = pload(g, 0);
-    bf16x8_t vbuf[kAhead];
-#pragma unroll
-    for (int i = 0; i < kAhead; ++i) vbuf[i] = vload(i);
+    constexpr int kAhead = kPvAhead;
+    bf16x8_t (&pb)[NW] = ops.pb;
+    bf16x8_t (&vbuf)[kAhead] = ops.vbuf;
+    auto vload = [&](int st) { return pv_vload(V, st); };
+    auto pload = [&](int g, int ks) { return pv_pload(Pb, g, ks); };
     static_for<kSteps>([&](auto sc) {
       constexpr int st = decltype(sc)::value;
       bf16x8_t v = vbuf[st % kAhead];
       in_vgpr(v);  // (at the use: the asm waits for the load)
       if constexpr (st + kAhead < kSteps) vbuf[st % kAhead] = vload(st + kAhead);
       const int db = st % kDimBlocks;
-#pragma unroll
-      for (int g = 0; g < NW; ++g) {
+      static_for<NW>([&](auto gc) {
+        constexpr int g = decltype(gc)::value;
         bf16x8_t b = pb[g];
         in_vgpr(b);
         o[g][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v, b, o[g][db], 0, 0, 0);
         // After its last use for the first key half, the group's operand
         // register takes the second half's (a pass of MFMAs ahead of use).
         if (st == kDimBlocks - 1) pb[g] = pload(g, 1);
-      }
-      extra(sc);  // work placed under this step's MFMAs
-      __builtin_amdgcn_sched_barrier(0);
+        extra(std::integral_constant<int, st * NW + g>{});  // work under this MFMA
+        __builtin_amdgcn_sched_barrier(0);
+      });
     });
   }
 
