@@ -224,11 +224,15 @@ hipError_t launch(const uint16_t* x, const uint16_t* w, uint16_t* out, int64_t T
                   hipStream_t stream) {
   if (T <= 0) return hipSuccess;
   if (H > 65535) return hipErrorInvalidValue;
-  // About four workgroups per compute unit (two resident at a time), each
-  // looping over token blocks with its staged weights.
+  // One round of workgroups (256 compute units; two resident workgroups per
+  // unit for the absorption, one for the up-projection), each looping over
+  // token blocks with its staged weights: a second round stages the weights
+  // again and leaves a tail (up-projection at T = 4096: 156 against 170 us
+  // with four workgroups per unit).
   const int64_t need = (T + kTok - 1) / kTok;
   constexpr int kNSplit = ProjShape<K, N>::kNSplit;
-  const int64_t per_head = std::max<int64_t>(1, 1024 / (static_cast<int64_t>(H) * kNSplit));
+  constexpr int64_t kSlots = ProjShape<K, N>::kStageOut ? 512 : 256;
+  const int64_t per_head = std::max<int64_t>(1, kSlots / (static_cast<int64_t>(H) * kNSplit));
   const int64_t blocks = std::min(need, per_head);
   const int64_t groups = (blocks * H + 7) / 8;  // of 8 (token-block, head) pairs
   const int64_t grid = groups * 8 * kNSplit;
