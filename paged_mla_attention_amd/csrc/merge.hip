@@ -100,6 +100,90 @@ __global__ __launch_bounds__(256) void split_merge_kernel(SplitMergeArgs a) {
   if (a.lse && lane == 0) a.lse[th] = wsum > 0.f ? M + logf(wsum) : -INFINITY;
 }
 
+// The same merge for few (token, head) pairs with many pieces each (a
+// long-context decode: 16 x 16 pairs of 32 pieces), where one wave per pair
+// leaves most compute units idle and each busy one with more rows in flight
+// than it can keep moving: one workgroup per pair, wave w taking pieces w,
+// w + 4, ... (kBatch rows per batch); every wave finds the pair's largest
+// LSE from all the pieces' LSEs, so the four partial sums share one scale,
+// and wave 0 adds them up through LDS.
+template <int kBatch>
+__global__ __launch_bounds__(256) void split_merge_wg_kernel(SplitMergeArgs a) {
+  __shared__ float part[3][64 * 8 + 64];  // waves 1..3: 8 sums per lane, then the weight sums
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int H = a.num_heads;
+  const int pair = blockIdx.x;
+  const int num_merges = a.num_merges_ptr ? *a.num_merges_ptr : a.num_merges;
+  if (pair >= num_merges * H) return;  // (uniform over the workgroup)
+  const int mi = pair / H, h = pair - mi * H;
+  const MergeItem m = a.merges ? a.merges[mi] : a.inline_merges[mi];
+  const int n = m.num_slots;
+  const int64_t base = static_cast<int64_t>(m.first_slot) * H + h;  // slot k: base + k H
+  const uint16_t* rows = a.part_o + base * kLoraRank + lane * 8;
+  const int64_t row_step = static_cast<int64_t>(H) * kLoraRank;
+  // Issued together: this wave's first batch of rows and the LSEs of pieces 0..63.
+  u32x4_t r[kBatch];
+#pragma unroll
+  for (int b = 0; b < kBatch; ++b) {
+    const int k = wave + 4 * b;
+    r[b] = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4_t*>(rows + (k < n ? k : n - 1) * row_step));
+  }
+  const float s_lane = lane < n ? a.part_lse[base + static_cast<int64_t>(lane) * H] : -INFINITY;
+  float M = s_lane;
+  for (int k = lane + 64; k < n; k += 64) M = fmaxf(M, a.part_lse[base + static_cast<int64_t>(k) * H]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (M != -INFINITY) {
+    for (int k0 = wave; k0 < n; k0 += 4 * kBatch) {
+      if (k0 > wave) {
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+          const int k = k0 + 4 * b;
+          r[b] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4_t*>(rows + (k < n ? k : n - 1) * row_step));
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int k = k0 + 4 * b;
+        const float s = k < 64 ? __shfl(s_lane, k < n ? k : 0)
+                               : a.part_lse[base + static_cast<int64_t>(k < n ? k : n - 1) * H];
+        const float w = (k >= n || s == -INFINITY) ? 0.f : expf(s - M);
+        wsum += w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[2 * j] += w * bf16_lo(r[b][j]);
+          acc[2 * j + 1] += w * bf16_hi(r[b][j]);
+        }
+      }
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) part[wave - 1][j * 64 + lane] = acc[j];
+    part[wave - 1][512 + lane] = wsum;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] += part[w][j * 64 + lane];
+    wsum += part[w][512 + lane];
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  const int64_t th = static_cast<int64_t>(m.token) * H + h;
+  u32x4_t o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    o[j] = to_bf16(acc[2 * j] * inv) | (static_cast<unsigned>(to_bf16(acc[2 * j + 1] * inv)) << 16);
+  __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(a.out + th * kLoraRank + lane * 8));
+  if (a.lse && lane == 0) a.lse[th] = wsum > 0.f ? M + logf(wsum) : -INFINITY;
+}
+
 __global__ __launch_bounds__(256) void merge_state_kernel(const uint16_t* v_a,
                                                           const float* s_a,
                                                           const uint16_t* v_b,
@@ -143,7 +227,14 @@ hipError_t launch_split_merge(const SplitMergeArgs& a, hipStream_t stream) {
   // (up to 4096 pairs, 16 waves per compute unit: residency does not limit
   // the round trips there)
   const bool few = pairs <= 4096;
-  if (few && a.max_pieces > 16)
+  // (at most 1024 pairs of more than 8 pieces: a workgroup per pair)
+  if (pairs <= 1024 && a.max_pieces > 8) {
+    const dim3 wg_grid(static_cast<unsigned>(pairs));
+    if (a.max_pieces > 16)
+      hipLaunchKernelGGL(split_merge_wg_kernel<8>, wg_grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL(split_merge_wg_kernel<4>, wg_grid, dim3(256), 0, stream, a);
+  } else if (few && a.max_pieces > 16)
     hipLaunchKernelGGL(split_merge_kernel<32>, grid, dim3(256), 0, stream, a);
   else if (few && a.max_pieces > 4)
     hipLaunchKernelGGL(split_merge_kernel<16>, grid, dim3(256), 0, stream, a);
