@@ -55,6 +55,9 @@
 //     unit in 80 KiB of LDS each; with an fp8 cache each of them adds a
 //     producer wave on an otherwise idle SIMD that loads and converts the
 //     codes while the computing wave runs the products (run_split);
+//   * at most 16 heads: those kernels hold 16 head slots on
+//     v_mfma_f32_16x16x32_bf16 instead (kH16), so no MFMA computes padding,
+//     and the probabilities stay in registers between the two products;
 //   * items covering a token's whole key range write bf16 output + LSE;
 //     pieces of a split token write normalised bf16 partials and their LSE,
 //     which a merge kernel combines.
@@ -72,6 +75,7 @@ typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
 typedef short s16x4_t __attribute__((vector_size(8)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __attribute__((address_space(4))) const int32_t const_i32_t;
@@ -180,9 +184,10 @@ __device__ __forceinline__ int opaque(int v) {
 // per compute unit for it): two ckv stages and two kpe slots with one tile
 // in flight.  With an fp8 cache the same layout serves the two-wave split
 // kernel (run_split), whose second wave fills the stages from the codes.
-template <int NW, bool kTileInPage, bool kFp8, bool kCompact>
+template <int NW, bool kTileInPage, bool kFp8, bool kCompact, bool kH16 = false>
 struct Attn {
   static_assert(!kCompact || NW == 1, "the compact variant is one wave");
+  static_assert(!kH16 || (NW == 1 && kCompact && !kFp8), "16 head slots: the compact layout");
   static_assert(!(kCompact && kFp8), "an fp8 cache with the compact layout runs run_split");
   // Tiles whose DMAs are in flight beyond the one being computed.
   static constexpr int kAhead = kCompact ? 1 : kTilesAhead;
@@ -238,6 +243,7 @@ struct Attn {
   int lane, l32, half, wave, head;
   bool head_ok;
   int ld_key, ld_off, qk_off_e, qk_off_o, pv_off0, pv_off1;  // per-lane LDS / row offsets
+  int k16_off0, k16_off1, v16_off_e, v16_off_o;      // (16 head slots)
   uint32_t lds_base;                               // LDS address of the stages
   float scale_log2;                                // sm_scale * log2(e)
   // current item
@@ -278,6 +284,24 @@ struct Attn {
     const int swz = kSwzA * par ^ kSwzB * cg;
     pv_off0 = pv_base + (((4 * g2 + (sl >> 2)) ^ swz) * 16);
     pv_off1 = pv_base + (((8 + 4 * g2 + (sl >> 2)) ^ swz) * 16);
+    if constexpr (kH16) {
+      // 16 head slots on v_mfma_f32_16x16x32_bf16 (lane l: slot l%16, lane
+      // group G = l/16).  Score operand of k-step ks (32 columns) and key
+      // half kh: key 16 kh + l%16, 8-column chunk dc = 4 ks + G, so the
+      // swizzle depends on G only and the k-step adds ks * 2048.
+      const int swz16 = kSwzA * (G & 1) ^ kSwzB * (G >> 1);
+      const int kb = (G >> 1) * 1024 + (G & 1) * 512;
+      k16_off0 = kb + (((sl) ^ swz16) * 16);
+      k16_off1 = kb + (((16 + sl) ^ swz16) * 16);
+      // P . V operand of 16-column block cb through the 16-lane transposing
+      // read: source lane s points at key 16 r + 4 G + s/4, columns
+      // 16 cb + 4 (s%4) .. +3 (chunk 2 cb + par, byte 8 (s%2) in it); read
+      // r = 1 is 256 bytes on, the block cb * 1024 on, and the chunk
+      // swizzle differs between even and odd blocks.
+      const int vb = par * 512 + (sl & 1) * 8;
+      v16_off_e = vb + ((((4 * G + (sl >> 2)) ^ (kSwzA * par))) * 16);
+      v16_off_o = vb + ((((4 * G + (sl >> 2)) ^ (kSwzA * par) ^ kSwzB)) * 16);
+    }
   }
 
   __device__ __forceinline__ char* pbuf(int t) const { return smem + kPOff + (t & 1) * kPBufBytes; }
@@ -732,16 +756,22 @@ struct Attn {
       const int ntiles = (kv_end - kv_begin + kTileKeys - 1) / kTileKeys;
 
       f32x16_t o[NW][kDimBlocks];
+      f32x4_t o16[32];          // (16 head slots)
       float m_ref = -INFINITY;  // reference max of scaled base-2 scores (per head)
       float m_seen = -INFINITY; // largest scaled score seen by this lane
       float l_run = 0.f;        // this lane's share of the softmax denominator
       for (;;) {
+        if constexpr (kH16) {
 #pragma unroll
-        for (int g = 0; g < NW; ++g)
+          for (int cb = 0; cb < 32; ++cb) o16[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        } else {
 #pragma unroll
-          for (int db = 0; db < kDimBlocks; ++db)
+          for (int g = 0; g < NW; ++g)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) o[g][db][j] = 0.f;
+            for (int db = 0; db < kDimBlocks; ++db)
+#pragma unroll
+              for (int j = 0; j < 16; ++j) o[g][db][j] = 0.f;
+        }
         l_run = 0.f;
         m_seen = -INFINITY;
         // Every wave is done with the previous item's (or attempt's) LDS.
@@ -774,6 +804,7 @@ struct Attn {
         // Query as the B operand of the 32x32x16 score MFMAs: lane (l32,
         // half) holds head 32 wave + l32, dims 16 ks + 8 half .. +8.
         u32x4_t q[kQSteps];
+        u32x4_t q16[kQ16];  // (16 head slots)
         if (!kQueryDirect) {
           const int qlane = opaque(lane);
 #pragma unroll
@@ -804,9 +835,15 @@ struct Attn {
           // Waited for here, with the first tiles issued before it: a wait
           // the compiler placed at the first use inside the key loop would
           // drain the DMAs in flight at every tile.
-          load_query(H, q);
+          if constexpr (kH16) {
+            load_query16(H, q16);
 #pragma unroll
-          for (int ks = 0; ks < kQSteps; ++ks) asm volatile("" : : "v"(q[ks]));
+            for (int ks = 0; ks < kQ16; ++ks) asm volatile("" : : "v"(q16[ks]));
+          } else {
+            load_query(H, q);
+#pragma unroll
+            for (int ks = 0; ks < kQSteps; ++ks) asm volatile("" : : "v"(q[ks]));
+          }
         }
         // The next tile's page id, read a tile ahead.
         int pg_next = kTileInPage ? page_at(min(cur_pl, n_pages - 1)) : 0;
@@ -837,6 +874,7 @@ struct Attn {
           const bool dma = t + kAhead < ntiles;
           const int base = kv_begin + t * kTileKeys;
           float x[16];
+          f32x4_t acc16[2];  // (16 head slots)
           PvOps pvo;  // operands of this wave's first P . V step (several waves)
           {
             TileDma d{};  // (defined on every path: a phi with undef would put it in VGPRs)
@@ -861,7 +899,7 @@ struct Attn {
             // a lane mask, rebuilt by VALU instructions in front of each DMA)
             const int dma_s = __builtin_amdgcn_readfirstlane(dma ? 1 : 0);
             if (!kPrepUnder && dma_s) prep();
-            scores(stage(t), kpe_slot(t), q, x, [&](auto kc) {
+            auto extra = [&](auto kc) {
               constexpr int k = decltype(kc)::value;
               // The first P . V operands of tile t-1 (published before this
               // iteration's barrier) go out under the chain's last k-steps,
@@ -877,10 +915,27 @@ struct Attn {
               } else {
                 dma_step<k>(d);
               }
-            });
+            };
+            if constexpr (kH16)
+              scores16(stage(t), kpe_slot(t), q16, acc16, extra);
+            else
+              scores(stage(t), kpe_slot(t), q, x, extra);
           }
           bf16x8_t p[2];
-          if (!kPipe || t == 0) {
+          if constexpr (kH16) {
+            // (one wave: the probabilities go straight into P . V)
+            float x8[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x8[j] = acc16[j >> 2][j & 3];
+            const float mx = softmax16_max(x8, base, m_seen);
+            if (t == 0) {
+              const float mh = slot_max16(mx);
+              if (m_ref == -INFINITY) m_ref = mh;  // O is still zero
+            }
+            bf16x8_t p16;
+            softmax16_exp(x8, -m_ref, l_run, p16);
+            pv16(stage(t), p16, o16);
+          } else if (!kPipe || t == 0) {
             const float mx = softmax_max(x, base, m_seen);
             if (t == 0) {
               const float mh = fmaxf(mx, __shfl_xor(mx, 32));
@@ -903,10 +958,12 @@ struct Attn {
               }
             });
           }
-          store_p(p, pbuf(t));
-          if (!kPipe) {
-            lds_barrier();
-            pv(stage(t), pbuf(t), o, [&](auto) {});
+          if constexpr (!kH16) {
+            store_p(p, pbuf(t));
+            if (!kPipe) {
+              lds_barrier();
+              pv(stage(t), pbuf(t), o, [&](auto) {});
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
           if constexpr (kFp8) {
@@ -933,10 +990,14 @@ struct Attn {
 #pragma unroll
         for (int w = 0; w < NW; ++w) any_redo |= flags[w];
         if (!any_redo) break;
-        m_ref = fmaxf(m_seen, __shfl_xor(m_seen, 32));  // the head's largest score
+        // the head's largest score
+        m_ref = kH16 ? slot_max16(m_seen) : fmaxf(m_seen, __shfl_xor(m_seen, 32));
       }
       if (e.pool_n > 0 && next >= e.w_end) pop();  // the next item comes from the pool
-      finish(o, m_ref, l_run);
+      if constexpr (kH16)
+        finish16(o16, m_ref, l_run);
+      else
+        finish(o, m_ref, l_run);
     }
     // Every read of the schedule (items, page lists) has been consumed by
     // every wave (a workgroup without items waits here for its entry DMA):
@@ -1055,9 +1116,13 @@ struct Attn {
       const int ntiles = (kv_end - kv_begin + kTileKeys - 1) / kTileKeys;
 
       f32x16_t o[NW][kDimBlocks];
+      f32x4_t o16[32];  // (16 head slots)
       float m_ref = -INFINITY, m_seen = -INFINITY, l_run = 0.f;
       for (;;) {
-        if constexpr (!producer) {
+        if constexpr (!producer && kH16) {
+#pragma unroll
+          for (int cb = 0; cb < 32; ++cb) o16[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        } else if constexpr (!producer) {
 #pragma unroll
           for (int db = 0; db < kDimBlocks; ++db)
 #pragma unroll
@@ -1106,6 +1171,29 @@ struct Attn {
             if (t + 2 < ntiles) raw_store(t + 2, ra);
             lds_barrier();  // (... and tile t+1)
           }
+        } else if constexpr (kH16) {
+          u32x4_t q16[kQ16];
+          load_query16(H, q16);
+#pragma unroll
+          for (int ks = 0; ks < kQ16; ++ks) asm volatile("" : : "v"(q16[ks]));
+          lds_barrier();  // tile 0 is in stage 0
+          for (int t = 0; t < ntiles; ++t) {
+            const int base = kv_begin + t * kTileKeys;
+            f32x4_t acc16[2];
+            scores16(stage(t), kpe_slot(t), q16, acc16, [&](auto) {});
+            float x8[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x8[j] = acc16[j >> 2][j & 3];
+            const float mx = softmax16_max(x8, base, m_seen);
+            if (t == 0) {
+              const float mh = slot_max16(mx);
+              if (m_ref == -INFINITY) m_ref = mh;  // O is still zero
+            }
+            bf16x8_t p16;
+            softmax16_exp(x8, -m_ref, l_run, p16);
+            pv16(stage(t), p16, o16);
+            lds_barrier();  // (tile t's stage is free; tile t+1 is in the other)
+          }
         } else {
           u32x4_t q[kQSteps];
           load_query(H, q);
@@ -1138,12 +1226,14 @@ struct Attn {
         lds_barrier();
         const int any_redo = __builtin_amdgcn_readfirstlane(flags[0]);
         if (!any_redo) break;
-        m_ref = fmaxf(m_seen, __shfl_xor(m_seen, 32));
+        m_ref = kH16 ? slot_max16(m_seen) : fmaxf(m_seen, __shfl_xor(m_seen, 32));
         lds_barrier();  // (the flag is read before the next attempt's barrier reuses the slot)
       }
       if (e.pool_n > 0 && next >= e.w_end) pop();
-      if constexpr (producer)
-        lds_barrier();  // (the one barrier of the finish)
+      if constexpr (producer) {
+        if constexpr (!kH16) lds_barrier();  // (the one barrier of the finish; finish16 has none)
+      } else if constexpr (kH16)
+        finish16(o16, m_ref, l_run);
       else
         finish(o, m_ref, l_run);
     }
@@ -1410,51 +1500,208 @@ struct Attn {
     else
       write_out(std::true_type{});
   }
+
+  // ---- At most 16 heads: one wave on v_mfma_f32_16x16x32_bf16 ----
+  // With 32 head slots on the 32x32x16 MFMA, half of every MFMA of a 16-head
+  // batch computed padding.  Here lane l holds head slot l%16 with lane
+  // group G = l/16, every product is a 16x16x32 MFMA of the same rate per
+  // flop, and the probabilities never leave the registers: the score
+  // accumulators of the two key halves (kh) give lane l the keys
+  // 16 kh + 4 G + j, which are the P^T operand of P . V once its k index
+  // 8 G + 4 r + j stands for key 16 r + 4 G + j, and the transposing V^T
+  // reads take their keys in that order.
+  static constexpr int kQ16 = kLatentDim / 32;  // k-steps of 32 over 576
+
+  // Query as the B operand: q[ks] of lane l is dims 32 ks + 8 G .. +8 of head
+  // slot l%16 (q_nope for ks < 16, q_pe after); head slots beyond H load
+  // head 0 and are never stored.
+  __device__ __forceinline__ void load_query16(int H, u32x4_t (&q)[kQ16]) const {
+    const int lane = opaque(this->lane);
+    const int hs = lane & 15, G = lane >> 4;
+    const int64_t h = static_cast<int64_t>(token) * H + (hs < H ? hs : 0);
+    const u32x4_t* qn = reinterpret_cast<const u32x4_t*>(a.q_nope + h * kLoraRank) + G;
+    const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(a.q_pe + h * kRopeDim) + G;
+#pragma unroll
+    for (int ks = 0; ks < kQ16; ++ks)
+      q[ks] = ks < kLoraRank / 32 ? qn[4 * ks] : qp[4 * (ks - kLoraRank / 32)];
+  }
+
+  // S^T of the tile in stage K / kpe slot Kpe: MFMA i is k-step i/2, key half
+  // i%2 (two accumulators, 36 MFMAs like the 32-slot chain, so the DMA
+  // schedule placed by extra(i) is the same); K operands read 3 MFMAs ahead.
+  // acc[kh][j] is the score of key 16 kh + 4 G + j for head slot l%16.
+  template <typename Extra>
+  __device__ __forceinline__ void scores16(const char* K, const char* Kpe,
+                                           const u32x4_t (&q)[kQ16], f32x4_t (&acc)[2],
+                                           Extra&& extra) const {
+    constexpr int kAheadK = 3;
+    const char* k0 = K + k16_off0;
+    const char* k1 = K + k16_off1;
+    const char* p0 = Kpe + k16_off0;
+    const char* p1 = Kpe + k16_off1;
+    auto kload = [&](int i) {
+      const int ks = i >> 1, kh = i & 1;
+      const char* b = ks < kLoraRank / 32 ? (kh ? k1 : k0) : (kh ? p1 : p0);
+      return *reinterpret_cast<const bf16x8_t*>(
+          b + (ks < kLoraRank / 32 ? ks : ks - kLoraRank / 32) * 2048);
+    };
+    bf16x8_t kbuf[kAheadK];
+#pragma unroll
+    for (int i = 0; i < kAheadK; ++i) kbuf[i] = kload(i);
+    acc[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    acc[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    static_for<2 * kQ16>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      bf16x8_t kv = kbuf[i % kAheadK];
+      in_vgpr(kv);
+      if constexpr (i + kAheadK < 2 * kQ16) kbuf[i % kAheadK] = kload(i + kAheadK);
+      acc[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          kv, __builtin_bit_cast(bf16x8_t, q[i >> 1]), acc[i & 1], 0, 0, 0);
+      extra(ic);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  }
+
+  // Softmax of the lane's 8 scores (x[4 kh + j]: key 16 kh + 4 G + j), as
+  // softmax_max / softmax_exp; the probabilities come out as the P^T operand.
+  __device__ __forceinline__ float softmax16_max(float (&x)[8], int base, float& m_seen) const {
+    if (__builtin_expect(base + kTileKeys > kv_end, 0)) {  // the item's last tile only
+      const int g4 = 4 * (opaque(lane) >> 4);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int key = base + 16 * (j >> 2) + g4 + (j & 3);
+        x[j] = key < kv_end ? x[j] : -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mx = fmaxf(mx, x[j]);
+    mx *= scale_log2;
+    m_seen = fmaxf(m_seen, mx);
+    return mx;
+  }
+  __device__ __forceinline__ void softmax16_exp(const float (&x)[8], float neg_ref, float& l_run,
+                                                bf16x8_t& p) const {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float v = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], scale_log2, neg_ref));
+      l_run += v;
+      p[j] = static_cast<__bf16>(v);
+    }
+  }
+  // The largest of a value over the four lanes of a head slot.
+  __device__ __forceinline__ static float slot_max16(float v) {
+    v = fmaxf(v, __shfl_xor(v, 16));
+    return fmaxf(v, __shfl_xor(v, 32));
+  }
+
+  // O^T += V^T . P^T for the tile in stage V: 32 column blocks of 16, one
+  // MFMA each (K = the tile's 32 keys), V^T read two blocks ahead.  o[cb][j]
+  // of lane l is column 16 cb + 4 G + j of head slot l%16.
+  __device__ __forceinline__ void pv16(const char* V, const bf16x8_t& p, f32x4_t (&o)[32]) const {
+    constexpr int kAheadV = 2;
+    const char* ve = V + v16_off_e;
+    const char* vo = V + v16_off_o;
+    auto vload = [&](int cb) {
+      const char* b = (cb & 1 ? vo : ve) + cb * 1024;
+      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(b));
+      const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(b + 256));
+      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8_t vbuf[kAheadV];
+#pragma unroll
+    for (int i = 0; i < kAheadV; ++i) vbuf[i] = vload(i);
+    static_for<32>([&](auto cc) {
+      constexpr int cb = decltype(cc)::value;
+      bf16x8_t v = vbuf[cb % kAheadV];
+      in_vgpr(v);
+      if constexpr (cb + kAheadV < 32) vbuf[cb % kAheadV] = vload(cb + kAheadV);
+      bf16x8_t b = p;
+      in_vgpr(b);
+      o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, b, o[cb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  }
+
+  // Writes the item's result (as finish): each lane stores its 4 columns of
+  // every block, scaled by 1/l of its head slot, as 8 bytes of bf16.
+  __device__ __forceinline__ void finish16(f32x4_t (&o)[32], float m_ref, float l_run) const {
+    const int lane = opaque(this->lane);
+    const int hs = lane & 15, G = lane >> 4;
+    float l_tot = l_run + __shfl_xor(l_run, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    const bool any = l_tot > 0.f;
+    const float inv = any ? a.out_scale / l_tot : 0.f;
+    const float lse_v = any ? (m_ref + __log2f(l_tot)) * kLn2 : -INFINITY;
+    const int H = a.num_heads;
+    const int64_t row0 = static_cast<int64_t>(slot >= 0 ? slot : token) * H;
+    float* dst_lse = slot >= 0 ? a.part_lse + row0 : (a.lse ? a.lse + row0 : nullptr);
+    if (dst_lse && hs < H && G == 0) dst_lse[hs] = lse_v;
+    if (hs >= H) return;
+    uint16_t* dst = (slot >= 0 ? a.part_o : a.out) + (row0 + hs) * kLoraRank + 4 * G;
+#pragma unroll
+    for (int cb = 0; cb < 32; ++cb) {
+      const f32x2_t lo = {o[cb][0] * inv, o[cb][1] * inv};
+      const f32x2_t hi = {o[cb][2] * inv, o[cb][3] * inv};
+      const u32x2_t w = {__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2_t)),
+                         __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, bf16x2_t))};
+      *reinterpret_cast<u32x2_t*>(dst + cb * 16) = w;
+    }
+  }
 };
 
-template <int NW, bool kTileInPage, bool kFp8, bool kCompact>
+template <int NW, bool kTileInPage, bool kFp8, bool kCompact, bool kH16 = false>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attention_kernel(AttnArgs args) {
   __shared__ __attribute__((aligned(1024)))
-  char smem[Attn<NW, kTileInPage, kFp8, kCompact>::kLdsBytes];
-  Attn<NW, kTileInPage, kFp8, kCompact> k(args, smem);
+  char smem[Attn<NW, kTileInPage, kFp8, kCompact, kH16>::kLdsBytes];
+  Attn<NW, kTileInPage, kFp8, kCompact, kH16> k(args, smem);
   k.run();
 }
 
 // fp8 cache, at most 32 heads, two workgroups per compute unit: a computing
 // and a producing wave per workgroup (Attn::run_split).
-template <bool kTileInPage>
+template <bool kTileInPage, bool kH16>
 __global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attention_split_kernel(AttnArgs args) {
-  __shared__ __attribute__((aligned(1024))) char smem[Attn<1, kTileInPage, false, true>::kLdsBytes];
-  Attn<1, kTileInPage, false, true> k(args, smem);
+  __shared__ __attribute__((aligned(1024)))
+  char smem[Attn<1, kTileInPage, false, true, kH16>::kLdsBytes];
+  Attn<1, kTileInPage, false, true, kH16> k(args, smem);
   k.run_split();
 }
 
-template <int NW, bool kFp8, bool kCompact = false>
+template <int NW, bool kFp8, bool kCompact = false, bool kH16 = false>
 hipError_t launch_nw(const AttnArgs& a, int num_workers, hipStream_t stream) {
   if (a.page_size % kTileKeys == 0)
-    hipLaunchKernelGGL((attention_kernel<NW, true, kFp8, kCompact>), dim3(num_workers),
+    hipLaunchKernelGGL((attention_kernel<NW, true, kFp8, kCompact, kH16>), dim3(num_workers),
                        dim3(NW * kWave), 0, stream, a);
   else
-    hipLaunchKernelGGL((attention_kernel<NW, false, kFp8, kCompact>), dim3(num_workers),
+    hipLaunchKernelGGL((attention_kernel<NW, false, kFp8, kCompact, kH16>), dim3(num_workers),
                        dim3(NW * kWave), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <bool kH16>
+hipError_t launch_split(const AttnArgs& a, int num_workers, hipStream_t stream) {
+  if (a.page_size % kTileKeys == 0)
+    hipLaunchKernelGGL((attention_split_kernel<true, kH16>), dim3(num_workers), dim3(2 * kWave), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((attention_split_kernel<false, kH16>), dim3(num_workers), dim3(2 * kWave),
+                       0, stream, a);
   return hipGetLastError();
 }
 
 template <bool kFp8>
 hipError_t launch_dtype(const AttnArgs& a, int num_workers, hipStream_t stream) {
   if (a.num_heads <= 32) {
+    // (at most 16 heads: the 16-slot layout of the same kernels)
     if constexpr (kFp8) {
       // (any worker count; the planner gives it two per compute unit)
-      if (a.page_size % kTileKeys == 0)
-        hipLaunchKernelGGL(attention_split_kernel<true>, dim3(num_workers), dim3(2 * kWave), 0,
-                           stream, a);
-      else
-        hipLaunchKernelGGL(attention_split_kernel<false>, dim3(num_workers), dim3(2 * kWave), 0,
-                           stream, a);
-      return hipGetLastError();
+      if (a.num_heads <= 16) return launch_split<true>(a, num_workers, stream);
+      return launch_split<false>(a, num_workers, stream);
     } else {
+      if (a.compact && a.num_heads <= 16) return launch_nw<1, false, true, true>(a, num_workers, stream);
       if (a.compact) return launch_nw<1, false, true>(a, num_workers, stream);
       return launch_nw<1, false>(a, num_workers, stream);
     }
