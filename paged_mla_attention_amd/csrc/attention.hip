@@ -52,12 +52,14 @@
 //     and page ids come from LDS, so nothing inside the key loop makes the
 //     in-order vmcnt drain the DMA queue;
 //   * at most 32 heads (one computing wave), two workgroups share a compute
-//     unit in 80 KiB of LDS each; with an fp8 cache each of them adds a
-//     producer wave on an otherwise idle SIMD that loads and converts the
-//     codes while the computing wave runs the products (run_split);
-//   * at most 16 heads: those kernels hold 16 head slots on
-//     v_mfma_f32_16x16x32_bf16 instead (kH16), so no MFMA computes padding,
-//     and the probabilities stay in registers between the two products;
+//     unit in 80 KiB of LDS each; with an fp8 cache (and a bf16 one of at
+//     most 16 heads) each of them adds a producer wave on an otherwise idle
+//     SIMD that loads the rows two tiles ahead into its registers and
+//     converts or copies them into the stages while the computing wave runs
+//     the products (run_split);
+//   * at most 16 heads: the computing wave holds 16 head slots on
+//     v_mfma_f32_16x16x32_bf16 (kH16), so no MFMA computes padding, and the
+//     probabilities stay in registers between the two products;
 //   * items covering a token's whole key range write bf16 output + LSE;
 //     pieces of a split token write normalised bf16 partials and their LSE,
 //     which a merge kernel combines.
@@ -182,12 +184,13 @@ __device__ __forceinline__ int opaque(int v) {
 // A compact one-wave variant (kCompact, bf16 stages only) in 80 KiB of LDS,
 // so that two workgroups share a compute unit (the host plans two workers
 // per compute unit for it): two ckv stages and two kpe slots with one tile
-// in flight.  With an fp8 cache the same layout serves the two-wave split
-// kernel (run_split), whose second wave fills the stages from the codes.
+// in flight.  With an fp8 cache (and a bf16 one of at most 16 heads) the
+// same layout serves the two-wave split kernel (run_split), whose second
+// wave fills the stages.
 template <int NW, bool kTileInPage, bool kFp8, bool kCompact, bool kH16 = false>
 struct Attn {
   static_assert(!kCompact || NW == 1, "the compact variant is one wave");
-  static_assert(!kH16 || (NW == 1 && kCompact && !kFp8), "16 head slots: the compact layout");
+  static_assert(!kH16 || (NW == 1 && kCompact && !kFp8), "16 head slots: the split kernel");
   static_assert(!(kCompact && kFp8), "an fp8 cache with the compact layout runs run_split");
   // Tiles whose DMAs are in flight beyond the one being computed.
   static constexpr int kAhead = kCompact ? 1 : kTilesAhead;
@@ -696,6 +699,7 @@ struct Attn {
   }
 
   __device__ void run() {
+    static_assert(!kH16, "16 head slots run in the split kernel");
     // A schedule in the host slot: the first item is read straight from
     // first_items (no dependent worker_indptr read) and, where it was staged,
     // its page list goes out to LDS now, with that read still in flight.
@@ -756,22 +760,16 @@ struct Attn {
       const int ntiles = (kv_end - kv_begin + kTileKeys - 1) / kTileKeys;
 
       f32x16_t o[NW][kDimBlocks];
-      f32x4_t o16[32];          // (16 head slots)
       float m_ref = -INFINITY;  // reference max of scaled base-2 scores (per head)
       float m_seen = -INFINITY; // largest scaled score seen by this lane
       float l_run = 0.f;        // this lane's share of the softmax denominator
       for (;;) {
-        if constexpr (kH16) {
 #pragma unroll
-          for (int cb = 0; cb < 32; ++cb) o16[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        } else {
+        for (int g = 0; g < NW; ++g)
 #pragma unroll
-          for (int g = 0; g < NW; ++g)
+          for (int db = 0; db < kDimBlocks; ++db)
 #pragma unroll
-            for (int db = 0; db < kDimBlocks; ++db)
-#pragma unroll
-              for (int j = 0; j < 16; ++j) o[g][db][j] = 0.f;
-        }
+            for (int j = 0; j < 16; ++j) o[g][db][j] = 0.f;
         l_run = 0.f;
         m_seen = -INFINITY;
         // Every wave is done with the previous item's (or attempt's) LDS.
@@ -804,7 +802,6 @@ struct Attn {
         // Query as the B operand of the 32x32x16 score MFMAs: lane (l32,
         // half) holds head 32 wave + l32, dims 16 ks + 8 half .. +8.
         u32x4_t q[kQSteps];
-        u32x4_t q16[kQ16];  // (16 head slots)
         if (!kQueryDirect) {
           const int qlane = opaque(lane);
 #pragma unroll
@@ -835,15 +832,9 @@ struct Attn {
           // Waited for here, with the first tiles issued before it: a wait
           // the compiler placed at the first use inside the key loop would
           // drain the DMAs in flight at every tile.
-          if constexpr (kH16) {
-            load_query16(H, q16);
+          load_query(H, q);
 #pragma unroll
-            for (int ks = 0; ks < kQ16; ++ks) asm volatile("" : : "v"(q16[ks]));
-          } else {
-            load_query(H, q);
-#pragma unroll
-            for (int ks = 0; ks < kQSteps; ++ks) asm volatile("" : : "v"(q[ks]));
-          }
+          for (int ks = 0; ks < kQSteps; ++ks) asm volatile("" : : "v"(q[ks]));
         }
         // The next tile's page id, read a tile ahead.
         int pg_next = kTileInPage ? page_at(min(cur_pl, n_pages - 1)) : 0;
@@ -874,7 +865,6 @@ struct Attn {
           const bool dma = t + kAhead < ntiles;
           const int base = kv_begin + t * kTileKeys;
           float x[16];
-          f32x4_t acc16[2];  // (16 head slots)
           PvOps pvo;  // operands of this wave's first P . V step (several waves)
           {
             TileDma d{};  // (defined on every path: a phi with undef would put it in VGPRs)
@@ -916,26 +906,10 @@ struct Attn {
                 dma_step<k>(d);
               }
             };
-            if constexpr (kH16)
-              scores16(stage(t), kpe_slot(t), q16, acc16, extra);
-            else
-              scores(stage(t), kpe_slot(t), q, x, extra);
+            scores(stage(t), kpe_slot(t), q, x, extra);
           }
           bf16x8_t p[2];
-          if constexpr (kH16) {
-            // (one wave: the probabilities go straight into P . V)
-            float x8[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) x8[j] = acc16[j >> 2][j & 3];
-            const float mx = softmax16_max(x8, base, m_seen);
-            if (t == 0) {
-              const float mh = slot_max16(mx);
-              if (m_ref == -INFINITY) m_ref = mh;  // O is still zero
-            }
-            bf16x8_t p16;
-            softmax16_exp(x8, -m_ref, l_run, p16);
-            pv16(stage(t), p16, o16);
-          } else if (!kPipe || t == 0) {
+          if (!kPipe || t == 0) {
             const float mx = softmax_max(x, base, m_seen);
             if (t == 0) {
               const float mh = fmaxf(mx, __shfl_xor(mx, 32));
@@ -958,12 +932,10 @@ struct Attn {
               }
             });
           }
-          if constexpr (!kH16) {
-            store_p(p, pbuf(t));
-            if (!kPipe) {
-              lds_barrier();
-              pv(stage(t), pbuf(t), o, [&](auto) {});
-            }
+          store_p(p, pbuf(t));
+          if (!kPipe) {
+            lds_barrier();
+            pv(stage(t), pbuf(t), o, [&](auto) {});
           }
           __builtin_amdgcn_sched_barrier(0);
           if constexpr (kFp8) {
@@ -990,14 +962,10 @@ struct Attn {
 #pragma unroll
         for (int w = 0; w < NW; ++w) any_redo |= flags[w];
         if (!any_redo) break;
-        // the head's largest score
-        m_ref = kH16 ? slot_max16(m_seen) : fmaxf(m_seen, __shfl_xor(m_seen, 32));
+        m_ref = fmaxf(m_seen, __shfl_xor(m_seen, 32));  // the head's largest score
       }
       if (e.pool_n > 0 && next >= e.w_end) pop();  // the next item comes from the pool
-      if constexpr (kH16)
-        finish16(o16, m_ref, l_run);
-      else
-        finish(o, m_ref, l_run);
+      finish(o, m_ref, l_run);
     }
     // Every read of the schedule (items, page lists) has been consumed by
     // every wave (a workgroup without items waits here for its entry DMA):
@@ -1020,24 +988,28 @@ struct Attn {
                          __HIP_MEMORY_SCOPE_SYSTEM);
   }
 
-  // fp8 cache, at most 32 heads: two waves per workgroup.  Wave 0 computes
-  // (scores, softmax, P . V and the finish of the compact one-wave kernel
-  // over its two bf16 stages); wave 1, on a SIMD the compact kernel leaves
-  // idle, produces: it loads each tile's E4M3 codes into its registers two
-  // tiles ahead and converts them, exactly, into the bf16 stage and kpe slot
-  // layout the computing wave reads.  One barrier per tile: behind it the
-  // producer has converted tile t+1 into the stage the computing wave
+  // fp8 cache with at most 32 heads, or bf16 cache with at most 16: two
+  // waves per workgroup.  Wave 0 computes (scores, softmax, P . V and the
+  // finish of the compact one-wave kernel over its two bf16 stages); wave 1,
+  // on a SIMD the compact kernel leaves idle, produces: it loads each tile's
+  // rows into its registers two tiles ahead and writes them into the bf16
+  // stage and kpe slot layout the computing wave reads (E4M3 codes
+  // converted, exactly; bf16 rows copied).  One barrier per tile: behind it
+  // the producer has filled tile t+1 into the stage the computing wave
   // finished with in tile t-1.  Used with the compact bf16 kernel's LDS
   // layout and launched with 128 threads.
+  template <bool kCodes>
   __device__ void run_split() {
     static_assert(NW == 1 && kCompact && !kFp8, "the split kernel uses the compact bf16 layout");
     // (one loop per role, so that neither carries the other's registers)
     if (wave == 1)
-      split_loop<true>();
+      split_loop<true, kCodes>();
     else
-      split_loop<false>();
+      split_loop<false, kCodes>();
   }
-  template <bool producer>
+  // kCodes: the cache holds fp8 codes (converted by the producer); else bf16
+  // rows, which the producer copies.
+  template <bool producer, bool kCodes>
   __device__ __forceinline__ void split_loop() {
     const bool fast_first = kTileInPage && a.first_items != nullptr;
     if (fast_first && producer && lane < kFirstPages)
@@ -1053,9 +1025,10 @@ struct Attn {
     };
     if (e.pool_n > 0 && e.w_begin == e.w_end) pop();
 
-    // Producer: this lane's key of a tile and which 16-column chunks of it
-    // (c = 2 j + half, j = 0 .. 17) it converts.
-    constexpr int kRawLoads = kLatentDim / 32;  // 18 x 16 bytes per lane
+    // Producer: this lane's key of a tile and which 16-byte pieces of its
+    // row it moves: piece 2 j + half (fp8: 16 columns, converted to two
+    // 8-column chunks; bf16: one 8-column chunk).
+    constexpr int kRawLoads = kCodes ? kLatentDim / 32 : kLatentDim / 16;  // 18 or 36 per lane
     typedef u32x4_t RawTile[kRawLoads];
     auto raw_load = [&](int t, int pg, RawTile& r) {
       const int key = min(kv_begin + t * kTileKeys + opaque(l32), kv_end - 1);
@@ -1067,13 +1040,24 @@ struct Attn {
         const int p = a.kv_indices[page_base + (P == 1 ? key : key / P)];
         row = P == 1 ? p : static_cast<int64_t>(p) * P + key % P;
       }
-      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.kv_cache8 + row * kLatentDim) + half;
+      const u32x4_t* src =
+          kCodes ? reinterpret_cast<const u32x4_t*>(a.kv_cache8 + row * kLatentDim) + half
+                 : reinterpret_cast<const u32x4_t*>(a.kv_cache + row * kLatentDim) + half;
 #pragma unroll
       for (int j = 0; j < kRawLoads; ++j) r[j] = src[2 * j];
     };
     auto raw_store = [&](int t, const RawTile& r) {
       char* stg = smem + (t % kNStages) * kCkvBytes;
       char* kp = smem + kKpeO + (t % kNKpe) * kKpeBytes;
+      if constexpr (!kCodes) {
+        // chunk dc = 2 j + half of the lane's key, as the DMA loader places it
+#pragma unroll
+        for (int j = 0; j < kRawLoads; ++j) {
+          char* dst = (j < kCkvDmas ? stg + j * 1024 : kp + (j - kCkvDmas) * 1024) + half * 512;
+          *reinterpret_cast<u32x4_t*>(dst + ((l32 ^ (kSwzA * half) ^ (kSwzB * (j & 1))) * 16)) = r[j];
+        }
+        return;
+      }
 #pragma unroll
       for (int j = 0; j < kRawLoads; ++j) {
         const int c = 2 * j + half;  // 16-column chunk of the lane's key
@@ -1659,15 +1643,16 @@ void attention_kernel(AttnArgs args) {
   k.run();
 }
 
-// fp8 cache, at most 32 heads, two workgroups per compute unit: a computing
-// and a producing wave per workgroup (Attn::run_split).
-template <bool kTileInPage, bool kH16>
+// fp8 cache with at most 32 heads (kCodes) or bf16 cache with at most 16,
+// two workgroups per compute unit: a computing and a producing wave per
+// workgroup (Attn::run_split).
+template <bool kTileInPage, bool kH16, bool kCodes>
 __global__ __launch_bounds__(2 * kWave) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attention_split_kernel(AttnArgs args) {
   __shared__ __attribute__((aligned(1024)))
   char smem[Attn<1, kTileInPage, false, true, kH16>::kLdsBytes];
   Attn<1, kTileInPage, false, true, kH16> k(args, smem);
-  k.run_split();
+  k.template run_split<kCodes>();
 }
 
 template <int NW, bool kFp8, bool kCompact = false, bool kH16 = false>
@@ -1681,14 +1666,14 @@ hipError_t launch_nw(const AttnArgs& a, int num_workers, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <bool kH16>
+template <bool kH16, bool kCodes>
 hipError_t launch_split(const AttnArgs& a, int num_workers, hipStream_t stream) {
   if (a.page_size % kTileKeys == 0)
-    hipLaunchKernelGGL((attention_split_kernel<true, kH16>), dim3(num_workers), dim3(2 * kWave), 0,
-                       stream, a);
+    hipLaunchKernelGGL((attention_split_kernel<true, kH16, kCodes>), dim3(num_workers),
+                       dim3(2 * kWave), 0, stream, a);
   else
-    hipLaunchKernelGGL((attention_split_kernel<false, kH16>), dim3(num_workers), dim3(2 * kWave),
-                       0, stream, a);
+    hipLaunchKernelGGL((attention_split_kernel<false, kH16, kCodes>), dim3(num_workers),
+                       dim3(2 * kWave), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -1698,10 +1683,12 @@ hipError_t launch_dtype(const AttnArgs& a, int num_workers, hipStream_t stream) 
     // (at most 16 heads: the 16-slot layout of the same kernels)
     if constexpr (kFp8) {
       // (any worker count; the planner gives it two per compute unit)
-      if (a.num_heads <= 16) return launch_split<true>(a, num_workers, stream);
-      return launch_split<false>(a, num_workers, stream);
+      if (a.num_heads <= 16) return launch_split<true, true>(a, num_workers, stream);
+      return launch_split<false, true>(a, num_workers, stream);
     } else {
-      if (a.compact && a.num_heads <= 16) return launch_nw<1, false, true, true>(a, num_workers, stream);
+      // (at most 16 heads: a producer wave stages the bf16 rows through its
+      // registers two tiles ahead, as for fp8 codes)
+      if (a.compact && a.num_heads <= 16) return launch_split<true, false>(a, num_workers, stream);
       if (a.compact) return launch_nw<1, false, true>(a, num_workers, stream);
       return launch_nw<1, false>(a, num_workers, stream);
     }

@@ -36,9 +36,9 @@ struct AttnArgs {
   // normalised output.
   float out_scale;
   // At most 32 heads: nonzero selects the compact kernels that run two
-  // workgroups per compute unit (one wave each; with an fp8 cache a
-  // computing and a producing wave each); the schedule must then have been
-  // made for two workers per compute unit.
+  // workgroups per compute unit (one wave each; with an fp8 cache, or at
+  // most 16 heads, a computing and a producing wave each); the schedule
+  // must then have been made for two workers per compute unit.
   int32_t compact;
   const float* scale_log2_ptr;  // non-null: read the scale here (reserved plans)
   // Schedule read from a pinned host slot: each workgroup stores run_seq to
