@@ -81,7 +81,7 @@ def test_fp8_long_decode_full():
     assert_close(o, lse, o_ref, l_ref, "fp8 long decode")
 
 
-@pytest.mark.parametrize("heads", [32, 128])
+@pytest.mark.parametrize("heads", [16, 32, 128])
 @pytest.mark.parametrize("page_size", [32, 33])
 def test_fp8_extreme_score_range_redo(heads, page_size):
     """Scores jumping by far more than 2^64 after an item's first tile (the

@@ -142,13 +142,14 @@ def _redo_items(w, sched, c_of_key, qscale):
     return n
 
 
-@pytest.mark.parametrize("heads", [32, 64, 128])
+@pytest.mark.parametrize("heads", [5, 16, 32, 64, 128])
 @pytest.mark.parametrize("page_size", [32, 33])
 def test_extreme_score_range_redo(heads, page_size):
     """Scores that jump by far more than 2^64 after a work item's first tile
     (the kernel's reference-maximum redo path) still match the oracle, in
-    every kernel instantiation (one, two and four waves; tiles inside pages
-    and tiles spanning pages), for a decode row and a causal prefill row.
+    every kernel instantiation (the two-wave kernel of 16 head slots, one,
+    two and four waves; tiles inside pages and tiles spanning pages), for a
+    decode row and a causal prefill row.
     The schedule is checked on the host to contain items that take the redo."""
     import paged_mla_attention_amd as pm
     rng = np.random.default_rng(17 + heads + page_size)
