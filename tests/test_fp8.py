@@ -167,7 +167,7 @@ def test_fp8_rejects_bad_scale():
             _run_fp8(w, codes, bad)
 
 
-@pytest.mark.parametrize("heads,page_size", [(128, 64), (32, 16)])
+@pytest.mark.parametrize("heads,page_size", [(128, 64), (32, 16), (16, 64)])
 def test_fp8_shared_pool_every_token(heads, page_size):
     """A batch with a shared pool of whole-token items over an fp8 cache:
     every token against the fp8 oracle, over two runs of one plan."""

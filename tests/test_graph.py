@@ -18,22 +18,24 @@ def _dev(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-@pytest.mark.parametrize("shape", ["decode", "prefill", "pool"])
-def test_graph_replays_match_eager(shape):
+@pytest.mark.parametrize("shape,heads", [("decode", 128), ("prefill", 128), ("pool", 128),
+                                         ("decode", 16), ("pool", 16)])
+def test_graph_replays_match_eager(shape, heads):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     import paged_mla_attention_amd as pm
     if shape == "decode":
-        w = W.make_workload("g_decode", 0, [700, 33, 1500, 64], [1, 1, 1, 1], 128, 64,
+        w = W.make_workload("g_decode", 0, [700, 33, 1500, 64], [1, 1, 1, 1], heads, 64,
                             rng=np.random.default_rng(41))
     elif shape == "pool":
         # enough query tokens (and small whole-token items) for the shared
         # pool, whose device counter every run must leave at zero
-        q_len = (4 * torch.cuda.get_device_properties(0).multi_processor_count + 7) // 8 + 3
+        workers = torch.cuda.get_device_properties(0).multi_processor_count * (2 if heads <= 32 else 1)
+        q_len = (4 * workers + 7) // 8 + 3
         kv = q_len + np.array([0, 1200, 40, 1500, 10, 900, 0, 1300])
-        w = W.make_workload("g_pool", 0, kv, [q_len] * 8, 128, 64, rng=np.random.default_rng(43))
+        w = W.make_workload("g_pool", 0, kv, [q_len] * 8, heads, 64, rng=np.random.default_rng(43))
     else:
-        w = W.make_workload("g_prefill", 0, [1200, 300, 2100], [256, 300, 128], 128, 64,
+        w = W.make_workload("g_prefill", 0, [1200, 300, 2100], [256, 300, 128], heads, 64,
                             rng=np.random.default_rng(42))
     T, H = w.num_tokens, w.num_heads
     qn, qp, kv = _dev(w.q_nope), _dev(w.q_pe), _dev(w.kv_cache)
