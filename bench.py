@@ -421,6 +421,8 @@ def main():
                     help="skip the long-decode and mixed-batch workloads")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the chunked-prefill workload (for profiling)")
+    ap.add_argument("--long-only", action="store_true",
+                    help="run only the long-context decode, bf16 then fp8 cache (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (for counter calibration)")
     ap.add_argument("--record-traffic", nargs=4, metavar="DIR",
@@ -442,6 +444,14 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+
+    if args.long_only:
+        wl = W.long_decode()
+        _, run_ms, _ = run_steps(wl, 50, 50, copies=1)
+        _, run8_ms, _ = run_steps(wl, 50, 50, copies=1, fp8_scale=0.05)
+        print(f"[bench] long decode: mla_run {run_ms * 1e3:.1f} us (bf16), "
+              f"{run8_ms * 1e3:.1f} us (fp8)", file=sys.stderr, flush=True)
         return
 
     if args.prefill_only:
