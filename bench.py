@@ -160,6 +160,31 @@ def run_steps(w, steps, warmup, copies=3, fp8_scale=None):
         full.append(time.perf_counter() - t1)
     torch.cuda.synchronize()
     stats["full_plan_host_us"] = round(float(np.median(full)) * 1e6, 1)
+    # Steps whose every plan is a full one (the two tables alternate), as in
+    # serving, where the batch changes each step: the host plans while the
+    # previous step's kernels run.
+    n_re = min(steps, 50)
+
+    def replan_step(k):
+        c = k % copies
+        plan.run(qns[c], qps[c], kvs[c], out=outs[c], lse=lses[c], kv_scale=fp8_scale)
+        plan.plan(qo, kvp, idx2 if k % 2 == 0 else idx, last, causal=w.causal,
+                  sm_scale=w.sm_scale, num_cache_pages=w.num_pages, kv_dtype=kv_dtype)
+
+    for k in range(10):
+        replan_step(k)
+    torch.cuda.synchronize()
+    gc.collect()
+    gc.disable()
+    t0 = time.perf_counter()
+    e0.record()
+    for k in range(n_re):
+        replan_step(k)
+    e1.record()
+    torch.cuda.synchronize()
+    stats["replan_step_us"] = round((time.perf_counter() - t0) / n_re * 1e6, 1)
+    gc.enable()
+    stats["replan_run_us"] = round(e0.elapsed_time(e1) / n_re * 1e3, 1)
     plan.close()
     return wall * 1e3, run_ms, stats
 
