@@ -112,8 +112,10 @@ mla_status mla_plan_create(mla_plan_t* out, int32_t device, int32_t num_heads,
  *
  * Errors: MLA_E_INVALID for a malformed table (indptr[0] != 0, decreasing
  * indptr, last_page_len outside [1, page_size] on a row with pages, page id
- * out of range, batch < 0, non-finite or non-positive sm_scale).  The plan
- * keeps its previous state on error. */
+ * out of range, batch < 0, non-finite or non-positive sm_scale);
+ * MLA_E_UNSUPPORTED when num_cache_pages * page_size exceeds 2^31 rows (the
+ * kernels address cache rows in 32 bits).  The plan keeps its previous state
+ * on error. */
 mla_status mla_plan(mla_plan_t plan, const int32_t* qo_indptr, const int32_t* kv_indptr,
                     const int32_t* kv_indices, const int32_t* kv_last_page_len,
                     int32_t batch, int32_t causal, float sm_scale,
@@ -263,8 +265,9 @@ mla_status mla_merge_state(const void* v_a, const float* s_a, const void* v_b,
  * including max_kv_len) yields zero output and -inf LSE for every token.
  *
  * Errors: MLA_E_INVALID for sizes beyond the limits, NULL pointers or a bad
- * scalar; MLA_E_UNSUPPORTED for num_heads outside [1, 128]; MLA_E_HIP when
- * the symbol lookup or a launch fails. */
+ * scalar; MLA_E_UNSUPPORTED for num_heads outside [1, 128] or
+ * num_cache_pages * page_size above 2^31 rows; MLA_E_HIP when the symbol
+ * lookup or a launch fails. */
 mla_status mla_run_noalloc(const int32_t* qo_indptr, const int32_t* kv_indptr,
                            const int32_t* kv_indices, const int32_t* kv_last_page_len,
                            int32_t batch, int64_t num_tokens, int64_t num_kv_indices,

@@ -355,6 +355,9 @@ extern "C" mla_status mla_run_noalloc(const int32_t* qo_indptr, const int32_t* k
     return na_fail(MLA_E_INVALID, "sm_scale must be finite and positive");
   if (batch < 0 || num_tokens < 0 || num_kv_indices < 0 || num_cache_pages < 0 || max_kv_len < 0)
     return na_fail(MLA_E_INVALID, "negative size");
+  // (cache rows, page * page_size + slot, are addressed in 32 bits)
+  if (num_cache_pages > (int64_t(INT32_MAX) + 1) / page_size)
+    return na_fail(MLA_E_UNSUPPORTED, "num_cache_pages * page_size exceeds 2^31 cache rows");
   if (batch > kNaMaxBatch || num_tokens > kNaMaxTokens) {
     std::snprintf(buf, sizeof buf,
                   "mla_run_noalloc takes at most %d rows and %d query tokens (got %d, %lld)",

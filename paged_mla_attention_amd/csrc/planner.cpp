@@ -142,6 +142,10 @@ mla_status build_schedule(const PlanArgs& a, Schedule* out) {
   if (a.batch > 0 && (!a.qo_indptr || !a.kv_indptr || !a.kv_last_page_len))
     return fail(MLA_E_INVALID, "NULL index array");
   if (a.num_cache_pages < 0) return fail(MLA_E_INVALID, "num_cache_pages must be >= 0");
+  // The kernels address a cache row (page * page_size + slot) in 32 bits;
+  // 2^31 bf16 rows are 2.5 TB, more than one device holds.
+  if (a.num_cache_pages > (int64_t(INT32_MAX) + 1) / a.page_size)
+    return fail(MLA_E_UNSUPPORTED, "num_cache_pages * page_size exceeds 2^31 cache rows");
 
   const int32_t B = a.batch;
   if (B > 0 && (a.qo_indptr[0] != 0 || a.kv_indptr[0] != 0))

@@ -72,3 +72,16 @@ def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         _native.load(str(tmp_path / "missing.so"))
     assert np.int32(0) == 0
+
+
+def test_noalloc_host_checks_before_touching_the_device(lib):
+    """mla_run_noalloc rejects bad scalars on the host, before its first HIP
+    call: a cache of more than 2^31 rows (the kernels address rows in 32
+    bits) and too many heads."""
+    l2 = _native.load(_native.LIB_PATH)
+    args = [None] * 4 + [1, 1, 1, 1, 0.1, (1 << 29) + 1, 64, 16, 4] + [None] * 6
+    assert l2.mla_run_noalloc(*args) == 2
+    assert b"2^31 cache rows" in l2.mla_last_error()
+    args[9], args[11] = 8, 129
+    assert l2.mla_run_noalloc(*args) == 2
+    assert b"num_heads" in l2.mla_last_error()

@@ -167,14 +167,14 @@ def test_plan_replay_matches_oracle(workers, host_lib):
 @pytest.mark.parametrize("bad,msg", [
     ("qo0", r"qo_indptr\[0\]"), ("kvdec", "kv_indptr decreases"), ("last0", "kv_last_page_len"),
     ("lastbig", "kv_last_page_len"), ("page", "kv_indices"), ("neg_page", "kv_indices"),
-    ("heads", "num_heads"),
+    ("heads", "num_heads"), ("rows", "2\\^31 cache rows"),
 ])
 def test_schedule_rejects_bad_tables(bad, msg, host_lib):
     qo = np.array([0, 1, 3], np.int32)
     kv = np.array([0, 2, 3], np.int32)
     idx = np.array([0, 1, 2], np.int32)
     last = np.array([3, 4], np.int32)
-    heads = 16
+    heads, pages = 16, 4
     if bad == "qo0":
         qo = np.array([1, 1, 3], np.int32)
     elif bad == "kvdec":
@@ -189,8 +189,10 @@ def test_schedule_rejects_bad_tables(bad, msg, host_lib):
         idx = np.array([0, -1, 2], np.int32)
     elif bad == "heads":
         heads = 129
+    elif bad == "rows":
+        pages = (1 << 29) + 1  # x 4 slots per page: one row past 2^31
     with pytest.raises(_native.MLAError, match=msg):
-        schedule(qo, kv, idx, last, 4, 4, heads, 8, lib_path=host_lib)
+        schedule(qo, kv, idx, last, 4, pages, heads, 8, lib_path=host_lib)
 
 
 def test_empty_batch(host_lib):
