@@ -1,8 +1,8 @@
 // Host planner: page-table validation and split-KV work balancing.
 //
 // The documentation describes planning on the host from CPU index tensors
-// (page "mstar.engine.resources.attn.flashinfer_mla", FlashInferMLAWrapper.plan:
-// "inputs may be CPU tensors") and a per-row key length built from
+// (page "mstar.engine.resources.attn.flashinfer_mla", FlashInferMLAWrapper.plan,
+// whose index inputs can be host tensors) and a per-row key length built from
 // paged_kv_indptr and paged_kv_last_page_len.  The split of long key ranges
 // into chunks, and their balance over compute units, is this library's own
 // design: the work is laid out as one stream of (token, key tile) units and
