@@ -1025,36 +1025,84 @@ struct Attn {
     };
     if (e.pool_n > 0 && e.w_begin == e.w_end) pop();
 
-    // Producer: this lane's key of a tile and which 16-byte pieces of its
-    // row it moves: piece 2 j + half (fp8: 16 columns, converted to two
-    // 8-column chunks; bf16: one 8-column chunk).
+    // Producer: which 16-byte pieces of a tile's rows a lane moves.  bf16
+    // rows go as whole 128-byte lines, eight keys per load, with
+    // non-temporal loads (each row is read once): load j (key group kg =
+    // j / 9, column group g = j % 9) gives lane L chunk 8 g + cx of key
+    // 8 kg + (L & 7), where cx spreads each 16-lane group over two chunks
+    // whose LDS swizzles differ, so that the copy into LDS has no bank
+    // conflict.  (Non-temporal loads of 32-byte pieces, 32 rows per load,
+    // would fetch every line once per piece.)  fp8 rows (576 bytes, not
+    // line-aligned) go as before: lane (l32, half) takes 16-column chunks
+    // 2 j + half of key l32, converted into two 8-column chunks.
     constexpr int kRawLoads = kCodes ? kLatentDim / 32 : kLatentDim / 16;  // 18 or 36 per lane
+    // (lane constants made again in each call, through opaque(): hoisted
+    // out of the tile loop they would hold registers the tiles need)
+    auto lane_key = [&] { return opaque(lane) & 7; };
+    auto lane_chunk = [&] {
+      const int ln = opaque(lane);
+      return 2 * ((ln >> 3) & 1) + ((ln >> 4) & 1) + 4 * (ln >> 5);
+    };
     typedef u32x4_t RawTile[kRawLoads];
     auto raw_load = [&](int t, int pg, RawTile& r) {
-      const int key = min(kv_begin + t * kTileKeys + opaque(l32), kv_end - 1);
+      const int base = kv_begin + t * kTileKeys;
+      const int rem = kv_end - 1 - base;  // keys past the item's end re-read its last key
       const int P = a.page_size;
-      int64_t row;
-      if (kTileInPage) {
-        row = static_cast<int64_t>(pg) * P + key % P;
-      } else {
-        const int p = a.kv_indices[page_base + (P == 1 ? key : key / P)];
-        row = P == 1 ? p : static_cast<int64_t>(p) * P + key % P;
-      }
-      const u32x4_t* src =
-          kCodes ? reinterpret_cast<const u32x4_t*>(a.kv_cache8 + row * kLatentDim) + half
-                 : reinterpret_cast<const u32x4_t*>(a.kv_cache + row * kLatentDim) + half;
+      if constexpr (kCodes) {
+        const int key = min(kv_begin + t * kTileKeys + opaque(l32), kv_end - 1);
+        int64_t row;
+        if (kTileInPage) {
+          row = static_cast<int64_t>(pg) * P + key % P;
+        } else {
+          const int p = a.kv_indices[page_base + (P == 1 ? key : key / P)];
+          row = P == 1 ? p : static_cast<int64_t>(p) * P + key % P;
+        }
+        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.kv_cache8 + row * kLatentDim) + half;
 #pragma unroll
-      for (int j = 0; j < kRawLoads; ++j) r[j] = src[2 * j];
+        for (int j = 0; j < kRawLoads; ++j) r[j] = src[2 * j];
+        return;
+      }
+      constexpr int kRowBytes = 2 * kLatentDim;
+      const int rk = lane_key(), rc = lane_chunk();
+      const char* cache = reinterpret_cast<const char*>(a.kv_cache);
+      if (kTileInPage) {
+        // (the tile stays in page pg: a uniform base and 32-bit lane offsets)
+        const char* sb = cache + (static_cast<int64_t>(pg) * P + base % P) * kRowBytes;
+        uint32_t off[4];
+#pragma unroll
+        for (int kg = 0; kg < 4; ++kg)
+          off[kg] = static_cast<uint32_t>(min(kg * 8 + rk, rem) * kRowBytes + rc * 16);
+#pragma unroll
+        for (int j = 0; j < kRawLoads; ++j)
+          r[j] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4_t*>(sb + off[j / 9] + (j % 9) * 128));
+      } else {
+        // (cache rows are below 2^31: the planner rejects larger caches)
+        int rows[4];
+#pragma unroll
+        for (int kg = 0; kg < 4; ++kg) {
+          const int key = base + min(kg * 8 + rk, rem);
+          const int p = a.kv_indices[page_base + (P == 1 ? key : key / P)];
+          rows[kg] = P == 1 ? p : p * P + key % P;
+        }
+#pragma unroll
+        for (int j = 0; j < kRawLoads; ++j)
+          r[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+              cache + static_cast<int64_t>(static_cast<uint32_t>(rows[j / 9])) * kRowBytes + rc * 16 +
+              (j % 9) * 128));
+      }
     };
     auto raw_store = [&](int t, const RawTile& r) {
       char* stg = smem + (t % kNStages) * kCkvBytes;
       char* kp = smem + kKpeO + (t % kNKpe) * kKpeBytes;
       if constexpr (!kCodes) {
-        // chunk dc = 2 j + half of the lane's key, as the DMA loader places it
+        // chunk dc of key kk, where the DMA loader places it
+        const int rk = lane_key(), rc = lane_chunk();
 #pragma unroll
         for (int j = 0; j < kRawLoads; ++j) {
-          char* dst = (j < kCkvDmas ? stg + j * 1024 : kp + (j - kCkvDmas) * 1024) + half * 512;
-          *reinterpret_cast<u32x4_t*>(dst + ((l32 ^ (kSwzA * half) ^ (kSwzB * (j & 1))) * 16)) = r[j];
+          const int kk = (j / 9) * 8 + rk, dc = 8 * (j % 9) + rc, blk = dc >> 1, hf = dc & 1;
+          char* dst = (blk < kCkvDmas ? stg + blk * 1024 : kp + (blk - kCkvDmas) * 1024) + hf * 512;
+          *reinterpret_cast<u32x4_t*>(dst + ((kk ^ (kSwzA * hf) ^ (kSwzB * (blk & 1))) * 16)) = r[j];
         }
         return;
       }
